@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with something independent of it: the H4 entries
+printed on the "INT8 Convrot Safetensors" page, numpy's Kronecker products and
+binary64 matmuls, closed forms, exact invariants, exact rational arithmetic
+with binary32 rounding written from the IEEE-754 definition, and brute-force
+integer loops.  The mutation test runs the same functions against broken
+copies of the oracle to show that each plausible mistake fails at least one.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle as oracle_pkg
+from oracle import fp64
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U32 = 2.0 ** -24            # unit roundoff of binary32
+
+
+def load_h4_golden() -> np.ndarray:
+    rows = []
+    with open(os.path.join(GOLDEN, "h4.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(v) for v in line.split()])
+    return np.array(rows) / 2.0
+
+
+def load_tie_row() -> tuple[np.ndarray, np.ndarray]:
+    vals, codes = [], []
+    with open(os.path.join(GOLDEN, "tie_row_g16.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                v, c = line.split()
+                vals.append(float(v))
+                codes.append(int(c))
+    return np.array(vals, dtype=np.float32), np.array(codes, dtype=np.int8)
+
+
+# ---------------------------------------------------------------- exact IEEE
+
+def rne_f32(q: Fraction) -> Fraction:
+    """Round an exact rational to the nearest binary32 value, ties to even.
+
+    Written from the definition: 24-bit significands for normal numbers,
+    fixed 2^-149 spacing below 2^-126.  Overflow is outside the tests' range.
+    """
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # now 2^e <= a < 2^(e+1)
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    k = a / ulp
+    fl = k.numerator // k.denominator
+    rem = k - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def round_half_even(q: Fraction) -> int:
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return int(fl)
+
+
+def F(x) -> Fraction:
+    return Fraction(float(x))
+
+
+# ----------------------------------------------------------------- the pins
+
+def pin_h4_entries(o):
+    """The G=4 rotation of the unit vectors is the page's H4, exactly."""
+    h4 = load_h4_golden()
+    assert np.array_equal(fp64.H4, h4), "fp64 helper H4 differs from the page's matrix"
+    R = o.rotate_rows(np.eye(4, dtype=np.float32), 4).astype(np.float64)
+    assert np.array_equal(R, h4), f"oracle G=4 rotation is not H4:\n{R}"
+
+
+def pin_kronecker_power(o):
+    """For G = 16, 64, 256 the butterfly equals the Kronecker power, exactly."""
+    for G in (16, 64, 256):
+        Rk = fp64.kron_power(G, load_h4_golden())
+        assert np.array_equal(Rk, fp64.closed_form(G)), f"kron chain != closed form, G={G}"
+        R = o.rotate_rows(np.eye(G, dtype=np.float32), G).astype(np.float64)
+        assert np.array_equal(R, Rk), f"oracle rotation != H4^(x)n for G={G}"
+
+
+def pin_orthogonal_symmetric(o):
+    """R R^T = I and R = R^T (exact); applying the oracle's rotation twice is
+    the identity on small-integer rows (all intermediates are dyadic)."""
+    for G in (4, 16, 256):
+        R = fp64.kron_power(G, load_h4_golden())
+        assert np.array_equal(R @ R.T, np.eye(G)), f"R R^T != I for G={G}"
+        assert np.array_equal(R, R.T), f"R not symmetric for G={G}"
+    rng = np.random.default_rng(11)
+    for G in (4, 16, 64, 256):
+        X = rng.integers(-8, 9, size=(6, 2 * G)).astype(np.float32)
+        Y = o.rotate_rows(o.rotate_rows(X, G), G)
+        assert np.array_equal(X, Y), f"rotation is not an involution, G={G}"
+
+
+def pin_constant_group(o):
+    """Regularity: a constant group rotates to itself, bit for bit."""
+    rng = np.random.default_rng(12)
+    for G in (4, 16, 64, 256):
+        c = (rng.standard_normal(8) * 10).astype(np.float32)
+        X = np.repeat(c, G).reshape(2, 4 * G)
+        assert np.array_equal(o.rotate_rows(X, G), X), f"constant groups moved, G={G}"
+
+
+def pin_one_hot(o):
+    """An isolated value v is spread to magnitude v / sqrt(G) on its whole group
+    (the rotation's stated purpose); the other groups stay zero."""
+    for G, v in ((16, 20.0), (256, 20.0), (256, -30.0)):
+        X = np.zeros((1, 2 * G), dtype=np.float32)
+        X[0, G + 5] = v
+        Y = o.rotate_rows(X, G)
+        assert np.all(Y[0, :G] == 0)
+        assert np.all(np.abs(Y[0, G:]) == np.float32(abs(v) / math.sqrt(G))), f"G={G}"
+        assert np.array_equal(np.sign(Y[0, G:]) * np.sign(v),
+                              np.sign(fp64.closed_form(G)[5])), f"sign pattern, G={G}"
+
+
+def pin_fp64_error_bound(o):
+    """Binary32 butterfly vs the dense binary64 R x: per group,
+    ||y - R x||_2 <= 5 n u ||x||_2 (first-order bound; each stage is orthogonal)."""
+    rng = np.random.default_rng(13)
+    for G in (16, 64, 256):
+        n = fp64.log4(G)
+        X = workloads.gaussian_activations(rng, 16, 4 * G, 0.01, 30.0, workloads.F32)
+        Y = o.rotate_rows(X, G).astype(np.float64)
+        Yd = fp64.rotate_dense(X, G)
+        err = np.linalg.norm((Y - Yd).reshape(-1, G), axis=1)
+        bound = 5 * n * U32 * np.linalg.norm(X.astype(np.float64).reshape(-1, G), axis=1)
+        assert np.all(err <= bound * 1.0001), f"G={G}: max err/bound {np.max(err / bound)}"
+        # and it is a genuine rounding error, not zero-by-accident
+        assert np.any(err > 0)
+
+
+def pin_fp64_identity(o):
+    """X_rot W_rot^T = X W^T in binary64 without quantization (the page's
+    identity, from R R^T = I); the binary64 butterfly also equals dense X R."""
+    rng = np.random.default_rng(14)
+    for (M, K, N, G) in ((8, 256, 32, 16), (64, 3072, 3072, 256)):
+        X = rng.standard_normal((M, K))
+        W = rng.standard_normal((N, K)) * 0.02
+        Xr = o.rotate_rows_f64(X, G)
+        Wr = o.rotate_rows_f64(W, G)
+        ref = X @ W.T
+        rel = np.max(np.abs(Xr @ Wr.T - ref)) / np.max(np.abs(ref))
+        assert rel <= 1e-12, f"identity violated ({M},{K},{N},G={G}): {rel}"
+        d = np.max(np.abs(Xr - fp64.rotate_dense(X, G))) / np.max(np.abs(X))
+        assert d <= 1e-14, f"binary64 butterfly != dense R: {d}"
+
+
+def pin_quantizer_invariants(o):
+    """Per row: the scale comes from the max over the WHOLE rotated row;
+    codes lie in [-127, 127] and reach +-127; |y - s q| <= s/2 (+ rounding)."""
+    rng = np.random.default_rng(15)
+    for G, K in ((16, 256), (256, 3072), (64, 512)):
+        X = workloads.gaussian_activations(rng, 33, K, 0.005, 30.0, workloads.F32)
+        X[7] = 0.0
+        p = o.quantize_rows(X, G)
+        Y = o.rotate_rows(X, G)
+        q, s = p.q.astype(np.int32), p.s
+        amax = np.max(np.abs(Y), axis=1)
+        assert np.array_equal(s, (amax / np.float32(127)).astype(np.float32)), "row scale"
+        assert np.all(np.abs(q) <= 127)
+        nz = amax > 0
+        assert np.all(np.max(np.abs(q[nz]), axis=1) == 127)
+        assert np.all(q[~nz] == 0) and np.all(s[~nz] == 0)
+        s64 = s.astype(np.float64)[:, None]
+        err = np.abs(Y.astype(np.float64) - s64 * q)
+        assert np.all(err <= s64 * (0.5 + 127 * 4 * U32)), "quantization error above s/2"
+
+
+def pin_quantizer_exact(o):
+    """Codes and scales against exact rational arithmetic with binary32
+    rounding at each step: s = fl(m / 127), inv = fl(127 / m),
+    q = round_half_even(fl(y * inv)) (readings: reciprocal, ties to even)."""
+    rng = np.random.default_rng(16)
+    X = workloads.gaussian_activations(rng, 4, 256, 0.01, 20.0, workloads.F32)
+    p = o.quantize_rows(X, 16)
+    Y = o.rotate_rows(X, 16)
+    for r in range(4):
+        m = F(np.max(np.abs(Y[r])))
+        assert F(p.s[r]) == rne_f32(m / 127), f"scale row {r}"
+        inv = rne_f32(Fraction(127) / m)
+        for i in range(256):
+            want = round_half_even(rne_f32(F(Y[r, i]) * inv))
+            want = max(-127, min(127, want))
+            assert int(p.q[r, i]) == want, f"code ({r},{i}): {p.q[r, i]} vs {want}"
+
+
+def pin_tie_row(o):
+    """Rounding rule, pinned on constructed ties (golden/tie_row_g16.txt)."""
+    vals, codes = load_tie_row()
+    X = np.repeat(vals, 16).reshape(1, 256).astype(np.float32)
+    p = o.quantize_rows(X, 16)
+    assert p.s[0] == np.float32(1.0)
+    assert np.array_equal(p.q[0], np.repeat(codes, 16)), f"{p.q[0][::16]} vs {codes}"
+    # the same row in bf16 (every value is exactly representable)
+    pb = o.quantize_rows(workloads.f32_to_bf16_bits(X), 16)
+    assert np.array_equal(pb.raw, p.raw)
+
+
+def pin_packed_layout(o):
+    """int8 [M_pad][K] codes, zero pad rows, then float [M_pad] scales (pad 0);
+    each row is quantized independently; the row stride is honoured."""
+    rng = np.random.default_rng(17)
+    M, K, G = 5, 256, 16
+    wide = workloads.gaussian_activations(rng, M, K + 64, 0.0, 1.0, workloads.F32)
+    X = np.ascontiguousarray(wide[:, :K])
+    p = o.quantize_rows(X, G)
+    assert p.raw.size == 8 * K + 4 * 8 == o.packed_bytes(M, K)
+    assert np.all(p.q_all[M:] == 0) and np.all(p.s_all[M:] == 0)
+    for r in range(M):
+        one = o.quantize_rows(X[r:r + 1], G)
+        assert np.array_equal(one.q[0], p.q[r]) and one.s[0] == p.s[r], f"row {r}"
+    strided = o.quantize_rows(wide, G, K=K)
+    assert np.array_equal(strided.raw, p.raw), "row stride"
+
+
+def pin_bf16_input(o):
+    """bf16 input quantizes exactly like its (exact) fp32 widening."""
+    rng = np.random.default_rng(18)
+    Xb = workloads.gaussian_activations(rng, 12, 1024, 0.005, 30.0, workloads.BF16)
+    Xf = workloads.bf16_bits_to_f32(Xb)
+    for G in (4, 64, 256):
+        assert np.array_equal(o.quantize_rows(Xb, G).raw, o.quantize_rows(Xf, G).raw), f"G={G}"
+
+
+def pin_input_scale(o):
+    """alpha pre-multiplies X once (binary32), and for alpha = 2^k the codes are
+    unchanged, the scale is scaled exactly and the output is bit-identical."""
+    rng = np.random.default_rng(19)
+    M, K, N, G = 9, 512, 40, 64
+    X = workloads.gaussian_activations(rng, M, K, 0.01, 20.0, workloads.F32)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    Qw, sw = o.weight_prep(W, G)
+    p1 = o.quantize_rows(X, G, 1.0)
+    for a in (0.5, 0.25, 4.0):
+        pa = o.quantize_rows(X, G, a)
+        assert np.array_equal(pa.q, p1.q), f"codes change at alpha={a}"
+        assert np.array_equal(pa.s, (p1.s * np.float32(a)).astype(np.float32)), f"alpha={a}"
+        assert np.array_equal(o.linear(X, G, Qw, sw, b, a), o.linear(X, G, Qw, sw, b, 1.0))
+    a = 0.3
+    pa = o.quantize_rows(X, G, a)
+    pre = (X * np.float32(a)).astype(np.float32)
+    assert np.array_equal(pa.raw, o.quantize_rows(pre, G, 1.0).raw), "pre-scale"
+
+
+def pin_gemm_bruteforce(o):
+    """int32 contraction vs pure-Python integer loops (non-square, so a
+    transposed operand cannot pass)."""
+    rng = np.random.default_rng(20)
+    M, K, N = 8, 256, 32
+    Qx = workloads.random_codes(rng, (M, K))
+    Qw = workloads.random_codes(rng, (N, K))
+    Qx[0, :] = 127
+    Qw[0, :] = -127
+    A = o.gemm_i32(Qx, Qw)
+    xl, wl = Qx.tolist(), Qw.tolist()
+    for r in range(M):
+        for c in range(N):
+            want = sum(a * b for a, b in zip(xl[r], wl[c]))
+            assert int(A[r, c]) == want, f"A[{r},{c}] = {A[r, c]} vs {want}"
+    # the int32 range guard
+    big = np.full((1, 133144), 127, dtype=np.int8)
+    assert int(o.gemm_i32(big, big)[0, 0]) == 133144 * 127 * 127
+    bigger = np.full((1, 133145), 127, dtype=np.int8)
+    try:
+        o.gemm_i32(bigger, bigger)
+    except oracle_pkg.OracleError:
+        pass
+    else:
+        raise AssertionError("int32 overflow not reported")
+
+
+def pin_epilogue_exact(o):
+    """Y = fl(fl(fl(fl(fl(A) * s_x) * s_w) / alpha) + b): exact rationals with
+    binary32 rounding per step, in the order the pages state."""
+    rng = np.random.default_rng(21)
+    M, N = 6, 40
+    A = rng.integers(-40_000_000, 40_000_000, size=(M, N)).astype(np.int32)
+    A[0, :4] = [0, 1, -1, 2 ** 24 + 1]
+    sx = workloads.random_scales(rng, M, 1e-3, 1e-1)
+    sw = workloads.random_scales(rng, N, 1e-4, 1e-2)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    for alpha in (1.0, 0.3):
+        Y = o.epilogue(A, sx, sw, b, alpha)
+        for r in range(M):
+            for c in range(N):
+                t = rne_f32(Fraction(int(A[r, c])))
+                t = rne_f32(t * F(sx[r]))
+                t = rne_f32(t * F(sw[c]))
+                if alpha != 1.0:
+                    t = rne_f32(t / F(np.float32(alpha)))
+                t = rne_f32(t + F(b[c]))
+                assert F(Y[r, c]) == t, f"Y[{r},{c}] alpha={alpha}"
+    # nullable scale and bias
+    Y = o.epilogue(A, sx, None, None)
+    assert F(Y[1, 3]) == rne_f32(rne_f32(Fraction(int(A[1, 3]))) * F(sx[1]))
+
+
+def pin_epilogue_fp64_bound(o):
+    """Independent of the order: |Y - Y64| <= 4u |A s_x s_w / alpha| + u |Y64|."""
+    rng = np.random.default_rng(22)
+    M, N = 16, 64
+    A = rng.integers(-50_000_000, 50_000_000, size=(M, N)).astype(np.int32)
+    sx = workloads.random_scales(rng, M)
+    sw = workloads.random_scales(rng, N, 1e-4, 1e-2)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    for alpha in (1.0, 0.5, 0.3):
+        Y = o.epilogue(A, sx, sw, b, alpha).astype(np.float64)
+        a32 = np.float64(np.float32(alpha))
+        P = A.astype(np.float64) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None] / a32
+        Y64 = P + b.astype(np.float64)[None]
+        assert np.all(np.abs(Y - Y64) <= 4.01 * U32 * np.abs(P) + 1.01 * U32 * np.abs(Y64))
+
+
+def pin_bf16_output(o):
+    """bf16 output is the fp32 result rounded to nearest, ties to even; exact
+    bf16 ties are constructed (257 lies halfway between 256 and 258)."""
+    A = np.array([[257, 259, 261, 263, -257, -259, 1, 65535, 65537, 12345678]], dtype=np.int32)
+    one = np.ones(1, dtype=np.float32)
+    Yb = o.epilogue(A, one, None, None, 1.0, oracle_pkg.BF16)
+    Yf = workloads.bf16_bits_to_f32(Yb)[0]
+    assert list(Yf[:6]) == [256.0, 260.0, 260.0, 264.0, -256.0, -260.0], Yf
+    rng = np.random.default_rng(23)
+    A = rng.integers(-2 ** 30, 2 ** 30, size=(8, 64)).astype(np.int32)
+    sx = workloads.random_scales(rng, 8)
+    Yf32 = o.epilogue(A, sx, None, None)
+    Yb = o.epilogue(A, sx, None, None, 1.0, oracle_pkg.BF16)
+    assert np.array_equal(Yb, workloads.f32_to_bf16_bits(Yf32))
+
+
+def pin_zero_row(o):
+    """An all-zero row has scale 0 and codes 0, so its output is the bias."""
+    rng = np.random.default_rng(24)
+    X = workloads.gaussian_activations(rng, 4, 256, 0.0, 1.0, workloads.F32)
+    X[2] = 0.0
+    W, b = workloads.gaussian_weights(rng, 16, 256)
+    Qw, sw = o.weight_prep(W, 16)
+    Y = o.linear(X, 16, Qw, sw, b)
+    assert np.array_equal(Y[2], b)
+
+
+def pin_rotation_reduces_error(o):
+    """Sanity of the method's stated purpose (not a parity gate): on inputs
+    with isolated outliers the G=256 rotation lowers the quantized output's
+    error against binary64 X W^T + b compared with no rotation (G = 1)."""
+    rng = np.random.default_rng(25)
+    X = workloads.gaussian_activations(rng, 32, 1024, 0.005, 30.0, workloads.F32)
+    W, b = workloads.gaussian_weights(rng, 64, 1024)
+    ref = X.astype(np.float64) @ W.T.astype(np.float64) + b
+    errs = {}
+    for G in (1, 256):
+        Qw, sw = o.weight_prep(W, G)
+        Y = o.linear(X, G, Qw, sw, b)
+        errs[G] = np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    assert errs[256] < 0.7 * errs[1], errs
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

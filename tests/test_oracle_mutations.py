@@ -1,0 +1,77 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Every mutation below is a plausible slip (a wrong sign, index, stride or
+constant, a dropped term, a swapped order, a wrong rounding rule) applied to
+the first occurrence of a line of ``oracle/convrot_oracle.c``.  The mutated
+copy is compiled with the oracle's own flags into a temporary directory; the
+real oracle is never modified.  All mutations keep every access in bounds.
+"""
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+MUTATIONS = {
+    "butterfly_sign": ("g[i] = h - x3;", "g[i] = h + x3;"),
+    "butterfly_index": ("g[i + st] = h - x2;", "g[i + st] = h - x1;"),
+    "butterfly_sum_term": ("float s = (x0 + x1) + (x2 + x3);", "float s = (x0 + x1) + (x2 - x3);"),
+    "butterfly_no_normalization": ("float h = s * 0.5f;", "float h = s;"),
+    "stage_stride": ("for (int st = 1; st < G; st *= 4)\n        h4_stage_f32",
+                     "for (int st = 1; st < G; st *= 16)\n        h4_stage_f32"),
+    "stage_skipped": ("for (int st = 1; st < G; st *= 4)\n        h4_stage_f32",
+                      "for (int st = 4; st < G; st *= 4)\n        h4_stage_f32"),
+    "f64_butterfly_sign": ("g[i + 3 * st] = h - x0;\n    }\n}\n\nstatic void rotate_group_f64",
+                           "g[i + 3 * st] = h + x0;\n    }\n}\n\nstatic void rotate_group_f64"),
+    "scale_constant": ("*s_out = m / 127.0f;", "*s_out = m / 128.0f;"),
+    "inverse_constant": ("float inv = 127.0f / m;", "float inv = 128.0f / m;"),
+    "round_truncate": ("float t = rintf(y[i] * inv);", "float t = truncf(y[i] * inv);"),
+    "round_half_away": ("float t = rintf(y[i] * inv);", "float t = roundf(y[i] * inv);"),
+    "per_group_max": ("for (int64_t i = 0; i < K; ++i) {\n        float a = fabsf(y[i]);",
+                      "for (int64_t i = 0; i < G; ++i) {\n        float a = fabsf(y[i]);"),
+    "prescale_divides": ("y[i] = y[i] * alpha;", "y[i] = y[i] / alpha;"),
+    "unscale_multiplies": ("t = t / alpha;", "t = t * alpha;"),
+    "unscale_after_bias": ("            if (alpha != 1.0f)\n                t = t / alpha;\n"
+                           "            if (bias)\n                t = t + bias[o];",
+                           "            if (bias)\n                t = t + bias[o];\n"
+                           "            if (alpha != 1.0f)\n                t = t / alpha;"),
+    "scale_order_swapped": ("            t = t * s_x[r];\n            if (s_w)\n                t = t * s_w[o];",
+                            "            if (s_w)\n                t = t * s_w[o];\n            t = t * s_x[r];"),
+    "gemm_reversed_index": ("acc += (int64_t)Qx[r * K + i] * (int64_t)Qw[o * K + i];",
+                            "acc += (int64_t)Qx[r * K + (K - 1 - i)] * (int64_t)Qw[o * K + i];"),
+    "gemm_dropped_term": ("for (int64_t i = 0; i < K; ++i)\n                acc +=",
+                          "for (int64_t i = 1; i < K; ++i)\n                acc +="),
+    "pack_tail_offset": ("uint8_t *tail = packed + m_pad * K;", "uint8_t *tail = packed + M * K;"),
+    "pad_rows_unwritten": ("            else\n                memset(Q + r * K, 0, (size_t)K);\n", "\n"),
+    "bf16_widen": ("uint32_t u = (uint32_t)((const uint16_t *)X)[idx] << 16;",
+                   "uint32_t u = (uint32_t)((const uint16_t *)X)[idx] << 15;"),
+    "bf16_round_half_up": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "zero_row_scale": ("        *s_out = 0.0f;\n        memset(q, 0, (size_t)K);\n        return;",
+                       "        m = 1.0f;"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation {name}: pattern not found"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / f"{name}.c"
+    c.write_text(mutated)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, str(c), "-o", str(so), "-lm"], check=True,
+                   capture_output=True)
+    return oracle.Oracle(str(so))
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    mutant = _build_mutant(tmp_path, name, old, new)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, oracle.OracleError) as e:
+            caught.append(pin.__name__)
+    assert caught, f"mutation {name} passed every pin"
