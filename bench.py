@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the INT8 convrot linear on one MI355X.
+
+One step is one pass of the whole hot path over one batch: the rotate +
+row-max + quantize + pack kernel over X, then the INT8 MFMA contraction with
+the fused reconstruction (scale, weight scale, unscale, bias, output cast).
+These are the two launches the fused entry convrot_int8_linear makes; the
+benchmark issues them as convrot_quantize_rows + int8_linear so that HIP
+events between them time each kernel over the timed region.  For the shared
+QKV workload a step is one convrot_int8_linear_shared call.
+
+Inputs are seeded synthetic DiT-shaped tensors (workloads.py), resident in
+HBM before timing starts.  Several input sets are rotated across steps so that
+the activations of a step are not still held in the 256 MiB Infinity Cache
+from an earlier step.  Weights are rotated and quantized on the GPU by the
+same library (convrot_quantize_rows on W) before timing.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on a single
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+MALL_BYTES = 256 << 20
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "gemm": os.path.join(ROOT, "int8_hadamard_rotated_amd", "csrc", "gemm_i8.hip"),
+    "quantize": os.path.join(ROOT, "int8_hadamard_rotated_amd", "csrc", "quantize.hip"),
+}
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def quantize_bytes(w: workloads.Workload) -> int:
+    """Algorithmic bytes of one quantize pass: read X once, write the packed tensor."""
+    esz = 2 if w.x_dtype == workloads.BF16 else 4
+    m_pad = (w.M + 3) // 4 * 4
+    return w.M * w.K * esz + m_pad * w.K + 4 * m_pad
+
+
+def gemm_ops(w: workloads.Workload, n_linears: int) -> int:
+    return 2 * w.M * w.N * w.K * n_linears
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the
+    kernel source still matches the one that was profiled."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kind}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def to_dev_x(X: np.ndarray, torch):
+    if X.dtype == np.uint16:
+        return torch.from_numpy(X.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    return torch.from_numpy(X).to("cuda:0")
+
+
+def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    the full layer (quantize, int32 contraction, reconstruction) for the first
+    `rows` rows of X against the full weight matrix."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    o = oracle.get()
+    Qw, sw = o.weight_prep(inp.W[0], w.G, threads=threads)          # untimed
+    yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
+    X = np.ascontiguousarray(inp.X[:rows])
+    t0 = time.perf_counter()
+    o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
+    dt = time.perf_counter() - t0
+    ops = 2 * rows * w.N * w.K
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {w.M} rows of {w.name} (quantize + int32 GEMM + reconstruction "
+                      f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp_up", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated over steps (0: enough to exceed the Infinity Cache)")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="rows in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the INT8 convrot linear is benchmarked on a "
+              "single MI355X (rows shard across GPUs with no exchange); --gpus must be 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_hadamard_rotated_amd as cr
+
+    w = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(w)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    # weights: rotated + quantized on the GPU by the library's own quantizer
+    lins = []
+    for W, b, a in zip(inp.W, inp.b, w.input_scales):
+        Wd = torch.from_numpy(W).to(dev)
+        packed = cr.convrot_quantize_rows(Wd, w.G)
+        Qw, sw = cr.packed_parts(packed, w.N, w.K)
+        lins.append(dict(Qw=Qw[: w.N], s_w=sw[: w.N], bias=torch.from_numpy(b).to(dev),
+                         input_scale=a))
+        del Wd
+    torch.cuda.synchronize()
+
+    yd = cr.BF16 if w.y_dtype == workloads.BF16 else cr.F32
+    ybytes = 2 if yd == cr.BF16 else 4
+    shared = w.n_linears > 1
+    n_packed = len(set(w.input_scales))
+    set_bytes = (inp.X.nbytes + cr.convrot_workspace_bytes(w.M, w.K, n_packed)
+                 + w.n_linears * w.M * w.N * ybytes)
+    n_sets = args.sets or max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for s in range(n_sets):
+        X = inp.X if s == 0 else workloads.make_inputs(w, seed=w.seed + 1000 * s).X
+        Xd = to_dev_x(X, torch)
+        ws = torch.empty(cr.convrot_workspace_bytes(w.M, w.K, n_packed), dtype=torch.uint8,
+                         device=dev)
+        Ys = [torch.empty((w.M, w.N), dtype=torch.bfloat16 if yd == cr.BF16 else torch.float32,
+                          device=dev) for _ in range(w.n_linears)]
+        sets.append((Xd, ws, Ys))
+    m_pad = (w.M + 3) // 4 * 4
+
+    def step(i, ev=None):
+        Xd, ws, Ys = sets[i % n_sets]
+        if shared:
+            if ev is not None:
+                ev[0].record()
+            cr.convrot_int8_linear_shared(
+                Xd, w.G, [dict(l, Y=Y) for l, Y in zip(lins, Ys)], workspace=ws)
+            if ev is not None:
+                ev[2].record()
+            return
+        l = lins[0]
+        if ev is not None:
+            ev[0].record()
+        cr.convrot_quantize_rows(Xd, w.G, l["input_scale"], packed=ws)
+        if ev is not None:
+            ev[1].record()
+        cr.int8_linear(ws[: m_pad * w.K].view(torch.int8).view(m_pad, w.K),
+                       ws[m_pad * w.K:m_pad * w.K + 4 * m_pad].view(torch.float32),
+                       l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    ops = gemm_ops(w, w.n_linears)
+    qbytes = quantize_bytes(w) * n_packed
+    rec = {
+        "metric": "int8 linear TOPS + quantize GB/s (fraction of MI355X roofline), M=4096 K=3072",
+        "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W i8 [{w.N},{w.K}] x "
+                               f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
+                               f"{list(w.input_scales)}",
+                   "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,
+                   "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets},
+    }
+    if not shared:
+        tq = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps * 1e-3
+        tg = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
+        q_gbs = quantize_bytes(w) / tq / 1e9
+        g_tops = ops / tg / 1e12
+        rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                           "us": round(tq * 1e6, 3), "bytes": quantize_bytes(w),
+                           "traffic": measured_traffic("quantize", w.name)}
+        rec["roofline"] = {"bound": "mfma", "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS,
+                           "unit": "TFLOP/s", "frac": round(g_tops / INT8_PEAK_TOPS, 4),
+                           "traffic": measured_traffic("gemm", w.name),
+                           "kernel": "gemm_i8 (contraction + fused reconstruction)",
+                           "us": round(tg * 1e6, 3),
+                           "note": "int8 ops: one multiply-add counts as 2"}
+    else:
+        tt = sum(e[0].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
+        rec["step_us_events"] = round(tt * 1e6, 3)
+        rec["roofline"] = None
+        rec["quantize"] = None
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

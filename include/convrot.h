@@ -1,0 +1,162 @@
+/*
+ * convrot.h -- C ABI of the MI355X (gfx950) INT8 convrot linear library.
+ *
+ * The layer (page "INT8 Convrot Safetensors", sd.cpp docs/int8_convrot.md,
+ * section "How INT8 convrot works"):
+ *
+ *   X_rot = X R            R = block-diagonal H4^(x)n over contiguous groups
+ *                          of G = 4^n input features, H4 = [[1,1,1,-1],
+ *                          [1,1,-1,1],[1,-1,1,1],[-1,1,1,1]] / 2
+ *   s_x[r] = max_i |X_rot[r,i]| / 127           (whole row; subsection
+ *   Q_x[r,i] = clamp(round(X_rot[r,i] / s_x[r]), -127, 127)   "Runtime
+ *                                                activation quantization")
+ *   A[r,o] = sum_i Q_x[r,i] * Q_w[o,i]          (int32)
+ *   Y[r,o] = A[r,o] * s_x[r] * s_w[o] + b[o]
+ *
+ * with Q_w, s_w the offline rotated and per-output-row quantized weights
+ * (subsection "Weight quantization"; the same quantizer applied to W's rows,
+ * so convrot_quantize_rows on W produces them).  For an input scale alpha != 1
+ * the activation is multiplied by alpha before the rotation and the output is
+ * divided by alpha before the bias; linears that share an input, the group size
+ * and alpha = 1 reuse one packed activation tensor (same section, last
+ * paragraph).  The operator-extensions page (sd.cpp docs/ggml_extensions.md,
+ * section "sd.cpp integration") fixes the reconstruction order
+ * float(A) * s_x * s_w + bias, the nullable weight scale and bias, and the
+ * packed layout (I8 rows padded to a multiple of four, then F32 row scales).
+ *
+ * Arithmetic contract (identical bits to the CPU oracle):
+ *   - the rotation is one H4 application per base-4 digit of the in-group
+ *     index, digit 0 (stride 1) first; each computes s = (x0 + x1) + (x2 + x3),
+ *     h = s * 0.5, y_j = h - x_{3-j}, every operation rounded to nearest even
+ *     binary32 (no contraction);
+ *   - s_x = fl(m / 127) with m = max |y| over the row; codes are
+ *     round-half-to-even(fl(y * fl(127 / m))) clamped to [-127, 127]
+ *     (the page's "/ s_x" is taken as a product with the row's correctly
+ *     rounded reciprocal); a row with m = 0 gets s_x = 0 and all-zero codes;
+ *   - Y = fl(fl(fl(fl(float(A)) * s_x) * s_w) / alpha) + b, each step rounded
+ *     separately (the division only when alpha != 1); bf16 output is rounded
+ *     to nearest even from that binary32 value.
+ *   - inputs must be finite, and every nonzero |x * alpha| must lie in
+ *     [2^-100, 2^100]; outside that range results are unspecified.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers unless stated otherwise; the caller owns all memory.
+ *     The library never allocates, frees or retains memory, and never
+ *     synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) in call order.
+ *   - Row-major, last index contiguous.  X is [M][ldx] (elements), W-side
+ *     codes Q_w are [N][K], Y is [M][ldy] (elements).
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a negative convrot_status is returned.
+ *     Errors are never retried and there is no fallback to another device.
+ *   - M = 0 or N = 0 is valid and enqueues nothing.
+ *   - GPU support: G in {4, 16, 64, 256}; K a multiple of 64 and of G; the
+ *     quantizer needs K <= 65536, the contraction K <= 133120 (so that
+ *     K * 127^2 < 2^31: codes are taken to lie in [-127, 127], as the
+ *     quantizer produces).  Pointers to X, packed buffers, Q_x, Q_w and the
+ *     workspace must be 16-byte aligned, ldx * sizeof(X element) a multiple
+ *     of 16; scale and bias pointers 4-byte aligned; Y aligned to its element.
+ *   - Concurrent calls that write the same buffers race; calls on one stream
+ *     are ordered.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONVROT_OK = 0,
+    CONVROT_EINVAL = -1,        /* null pointer, bad shape/stride/alignment, bad input scale */
+    CONVROT_EUNSUPPORTED = -2,  /* group size, K granularity or dtype not supported */
+    CONVROT_EOVERFLOW = -3,     /* K too large for an exact int32 accumulator */
+    CONVROT_EOVERLAP = -4,      /* an output overlaps a buffer the same kernel reads */
+    CONVROT_EWORKSPACE = -5,    /* workspace missing or smaller than required */
+    CONVROT_EHIP = -6           /* the HIP runtime reported an error at launch */
+} convrot_status;
+
+typedef enum { CONVROT_F32 = 0, CONVROT_BF16 = 1 } convrot_dtype;
+
+/* Bytes of the packed activation tensor for M rows of K features:
+ * int8 codes [M_pad][K] followed by float scales [M_pad], M_pad = 4*ceil(M/4).
+ * Pad rows hold zero codes and a zero scale.  Returns 0 if M < 0 or K < 1. */
+size_t convrot_packed_bytes(int64_t M, int64_t K);
+
+/* Rotate, quantize and pack M rows of X.
+ *   X           [M][ldx] f32 or bf16 (x_dtype), first K columns used
+ *   group_size  G, rotation group (power of four dividing K)
+ *   input_scale alpha > 0, finite; X is multiplied by it before the rotation
+ *   packed      convrot_packed_bytes(M, K) bytes, written entirely (pad rows
+ *               and pad scales included); must not overlap X
+ * Returns CONVROT_OK or a negative status (nothing enqueued on error). */
+int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          int group_size, float input_scale, void *packed, void *stream);
+
+/* INT8 linear on already-quantized activations (the GEMM + reconstruction):
+ *   Y = fl(fl(fl(fl(float(Q_x Q_w^T)) * s_x) * s_w) / input_scale) + bias
+ *   Qx     [M][K] int8 codes (row stride K); for a packed tensor pass its base
+ *   s_x    [M] float row scales; for a packed tensor pass base + M_pad * K
+ *   Qw     [N][K] int8 weight codes
+ *   s_w    [N] float weight scales, or NULL (taken as 1, no multiply)
+ *   bias   [N] float, or NULL (no add)
+ *   input_scale  the divisor alpha (1 = no division)
+ *   Y      [M][ldy] f32 or bf16 (y_dtype); must not overlap any input
+ */
+int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+                const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
+                int y_dtype, int64_t ldy, void *stream);
+
+/* Workspace bytes needed by the fused entries for `n_packed` packed tensors of
+ * M rows x K features (each rounded up to 256 bytes). */
+size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed);
+
+/* The fused layer for one linear: convrot_quantize_rows into the workspace,
+ * then int8_linear on it.  workspace >= convrot_workspace_bytes(M, K, 1);
+ * contents are not preserved between calls.  Y may alias X (X is fully
+ * consumed before Y is written) but not Qw, s_w, bias or the workspace. */
+int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        int group_size, float input_scale, const int8_t *Qw, const float *s_w,
+                        const float *bias, int64_t N, void *Y, int y_dtype, int64_t ldy,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* One linear reading a shared input (host-side descriptor). */
+typedef struct {
+    const int8_t *Qw;     /* [N][K] int8 weight codes (device) */
+    const float *s_w;     /* [N] or NULL (device) */
+    const float *bias;    /* [N] or NULL (device) */
+    int64_t N;            /* output features */
+    float input_scale;    /* alpha of this linear */
+    void *Y;              /* [M][ldy] output (device) */
+    int y_dtype;          /* CONVROT_F32 or CONVROT_BF16 */
+    int64_t ldy;          /* output row stride in elements (>= N) */
+} convrot_linear_desc;
+
+/* Several linears on the same X and group size.  Every distinct input scale
+ * gets one quantization pass (all alpha = 1 linears share one packed tensor,
+ * as the page prescribes; linears with equal alpha != 1 also share, which
+ * gives the same bits as separate passes); then one grouped GEMM launch per
+ * packed tensor covers all linears that read it.  descs is host memory,
+ * 1 <= n <= 16; workspace >= convrot_workspace_bytes(M, K, distinct scales).
+ * Outputs must not overlap each other, any weight-side input or the workspace. */
+int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               int group_size, int n, const convrot_linear_desc *descs,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* The raw int32 accumulator A = Q_x Q_w^T (same contraction kernel as
+ * int8_linear, with the reconstruction replaced by an int32 store); for
+ * checking the contraction bit for bit.  A is [M][N] int32. */
+int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
+                          int32_t *A, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *convrot_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -1,0 +1,241 @@
+"""MI355X (gfx950) INT8 convrot linear: Python binding over libconvrot.so.
+
+Every entry point has the name and meaning of its C counterpart in
+``include/convrot.h``; this module only marshals torch tensors (device
+pointers) and the current HIP stream into those calls and raises on a
+non-zero status.  All computation happens in the library's HIP kernels; there
+is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libconvrot.so")
+
+OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+MAX_LINEARS = 16
+
+_lib = None
+
+
+class ConvrotError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({convrot_status_string(status)})")
+
+
+class LinearDesc(ctypes.Structure):
+    """Mirror of convrot_linear_desc."""
+    _fields_ = [
+        ("Qw", ctypes.c_void_p),
+        ("s_w", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("N", ctypes.c_int64),
+        ("input_scale", ctypes.c_float),
+        ("Y", ctypes.c_void_p),
+        ("y_dtype", ctypes.c_int),
+        ("ldy", ctypes.c_int64),
+    ]
+
+
+def library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libconvrot.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with int8_hadamard_rotated_amd._build.build()"
+                           " (or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    i64, i32, f32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    sigs = {
+        "convrot_packed_bytes": (sz, [i64, i64]),
+        "convrot_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp]),
+        "int8_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
+        "convrot_workspace_bytes": (sz, [i64, i64, i32]),
+        "convrot_int8_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
+                                      i64, vp, sz, vp]),
+        "convrot_int8_linear_shared": (i32, [vp, i32, i64, i64, i64, i32, i32,
+                                             ctypes.POINTER(LinearDesc), vp, sz, vp]),
+        "convrot_int8_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
+        "convrot_status_string": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return {F32: torch.float32, BF16: torch.bfloat16}[code]
+
+
+def _row_stride(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with a contiguous last dimension")
+    return t.stride(0)
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise ConvrotError(fn, status)
+
+
+# -------------------------------------------------------------- the entries
+
+def convrot_status_string(status: int) -> str:
+    return library().convrot_status_string(status).decode()
+
+
+def convrot_packed_bytes(M: int, K: int) -> int:
+    return int(library().convrot_packed_bytes(M, K))
+
+
+def convrot_workspace_bytes(M: int, K: int, n_packed: int) -> int:
+    return int(library().convrot_workspace_bytes(M, K, n_packed))
+
+
+def packed_parts(packed, M: int, K: int):
+    """Views of a packed tensor: (codes int8 [M_pad, K], scales float32 [M_pad])."""
+    torch = _torch()
+    m_pad = (M + 3) // 4 * 4
+    q = packed[: m_pad * K].view(torch.int8).view(m_pad, K)
+    s = packed[m_pad * K: m_pad * K + 4 * m_pad].view(torch.float32)
+    return q, s
+
+
+def convrot_quantize_rows(X, group_size: int, input_scale: float = 1.0, packed=None,
+                          K: int | None = None, stream=None):
+    """Rotate, quantize and pack the rows of X (first K columns); returns the
+    packed uint8 tensor (allocated if not given)."""
+    torch = _torch()
+    M = X.shape[0]
+    ldx = _row_stride(X) if M > 0 else X.shape[1]
+    K = X.shape[1] if K is None else K
+    if packed is None:
+        packed = torch.empty(convrot_packed_bytes(M, K), dtype=torch.uint8, device=X.device)
+    rc = library().convrot_quantize_rows(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
+                                         ctypes.c_float(input_scale), _ptr(packed), _stream(stream))
+    _check("convrot_quantize_rows", rc)
+    return packed
+
+
+def int8_linear(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, Y=None,
+                y_dtype: int = F32, M: int | None = None, stream=None):
+    """Y = reconstruction of Q_x Q_w^T (Qx [M, K] int8 rows, s_x [M])."""
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = Qw.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=Qw.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    rc = library().int8_linear(_ptr(Qx), _ptr(s_x), M, K, _ptr(Qw), _ptr(s_w), _ptr(bias), N,
+                               ctypes.c_float(input_scale), _ptr(Y), _dtype_code(Y), ldy,
+                               _stream(stream))
+    _check("int8_linear", rc)
+    return Y
+
+
+def convrot_int8_gemm_i32(Qx, Qw, A=None, M: int | None = None, stream=None):
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = Qw.shape[0]
+    if A is None:
+        A = torch.empty((M, N), dtype=torch.int32, device=Qw.device)
+    rc = library().convrot_int8_gemm_i32(_ptr(Qx), _ptr(Qw), M, K, N, _ptr(A), _stream(stream))
+    _check("convrot_int8_gemm_i32", rc)
+    return A
+
+
+def convrot_int8_linear(X, group_size: int, input_scale: float, Qw, s_w=None, bias=None, Y=None,
+                        y_dtype: int = F32, workspace=None, stream=None):
+    torch = _torch()
+    M, K = X.shape
+    N = Qw.shape[0]
+    ldx = _row_stride(X) if M > 0 else K
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=Qw.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_workspace_bytes(M, K, 1), 1), dtype=torch.uint8,
+                                device=X.device)
+    rc = library().convrot_int8_linear(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
+                                       ctypes.c_float(input_scale), _ptr(Qw), _ptr(s_w), _ptr(bias),
+                                       N, _ptr(Y), _dtype_code(Y), ldy, _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    _check("convrot_int8_linear", rc)
+    return Y
+
+
+def convrot_int8_linear_shared(X, group_size: int, linears, workspace=None, stream=None):
+    """``linears``: sequence of dicts with keys Qw, s_w, bias, input_scale and
+    optionally Y / y_dtype.  Returns the list of outputs."""
+    torch = _torch()
+    M, K = X.shape
+    ldx = _row_stride(X) if M > 0 else K
+    n = len(linears)
+    descs = (LinearDesc * max(n, 1))()
+    outs = []
+    scales = []
+    for i, lin in enumerate(linears):
+        Qw = lin["Qw"]
+        N = Qw.shape[0]
+        Y = lin.get("Y")
+        if Y is None:
+            Y = torch.empty((M, N), dtype=_torch_dtype(lin.get("y_dtype", F32)), device=Qw.device)
+        outs.append(Y)
+        a = float(lin.get("input_scale", 1.0))
+        if a not in scales:
+            scales.append(a)
+        descs[i].Qw = Qw.data_ptr()
+        descs[i].s_w = lin["s_w"].data_ptr() if lin.get("s_w") is not None else None
+        descs[i].bias = lin["bias"].data_ptr() if lin.get("bias") is not None else None
+        descs[i].N = N
+        descs[i].input_scale = a
+        descs[i].Y = Y.data_ptr()
+        descs[i].y_dtype = _dtype_code(Y)
+        descs[i].ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_workspace_bytes(M, K, len(scales)), 1),
+                                dtype=torch.uint8, device=X.device)
+    rc = library().convrot_int8_linear_shared(_ptr(X), _dtype_code(X), M, K, ldx, group_size, n,
+                                              descs, _ptr(workspace), workspace.numel(),
+                                              _stream(stream))
+    _check("convrot_int8_linear_shared", rc)
+    return outs

@@ -1,0 +1,373 @@
+// C ABI of the INT8 convrot linear library: host-side validation, workspace
+// carving and kernel dispatch.  Semantics and conventions are documented in
+// include/convrot.h.  Nothing here allocates device memory or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/convrot.h"
+#include "kernels.h"
+
+using namespace convrot_detail;
+
+namespace {
+
+constexpr int64_t kMaxContractionK = 133120;   // largest multiple of 64 with K * 127^2 < 2^31
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Span span_of(const void *p, int64_t bytes)
+{
+    Span s;
+    if (p && bytes > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + (uintptr_t)bytes;
+    }
+    return s;
+}
+
+// Bytes touched by `rows` rows of `cols` elements at row stride `ld` elements.
+Span rows_span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem)
+{
+    if (rows <= 0 || cols <= 0)
+        return Span{};
+    return span_of(p, ((rows - 1) * ld + cols) * elem);
+}
+
+bool overlap(Span a, Span b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
+
+int64_t elem_bytes(int dtype) { return dtype == CONVROT_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == CONVROT_F32 || dtype == CONVROT_BF16; }
+
+bool scale_ok(float a) { return std::isfinite(a) && a > 0.0f; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_EHIP; }
+
+// Group size rule of the convrot checkpoint format (a power of four dividing
+// K), restricted to the groups this library implements, plus the MFMA K
+// granularity of 64.
+int check_quantizer_shape(int64_t K, int G)
+{
+    if (!(G == 4 || G == 16 || G == 64 || G == 256))
+        return CONVROT_EUNSUPPORTED;
+    if (K % 64 != 0 || K % G != 0)
+        return CONVROT_EUNSUPPORTED;
+    if (K > quantize_max_k(K))
+        return CONVROT_EUNSUPPORTED;
+    return CONVROT_OK;
+}
+
+int check_quantize_args(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                        float alpha)
+{
+    if (M < 0 || K < 1 || ldx < K)
+        return CONVROT_EINVAL;
+    if (!dtype_ok(x_dtype))
+        return CONVROT_EUNSUPPORTED;
+    const int rc = check_quantizer_shape(K, G);
+    if (rc != CONVROT_OK)
+        return rc;
+    if (!scale_ok(alpha))
+        return CONVROT_EINVAL;
+    if (M > 0 && (!X || !aligned(X, 16) || (ldx * elem_bytes(x_dtype)) % 16 != 0))
+        return CONVROT_EINVAL;
+    return CONVROT_OK;
+}
+
+struct LinearCheck {
+    Span y, reads;   // reads: the weight-side inputs (Qw, s_w, bias)
+    Span qw, sw, b;
+};
+
+int check_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t M, int64_t K,
+                 int64_t N, float alpha, const void *Y, int y_dtype, int64_t ldy, bool need_scales,
+                 LinearCheck *out)
+{
+    if (N < 0 || ldy < N)
+        return CONVROT_EINVAL;
+    if (need_scales && !dtype_ok(y_dtype))
+        return CONVROT_EUNSUPPORTED;
+    if (!scale_ok(alpha))
+        return CONVROT_EINVAL;
+    if (M > 0 && N > 0) {
+        if (!Qw || !Y || !aligned(Qw, 16))
+            return CONVROT_EINVAL;
+        if ((s_w && !aligned(s_w, 4)) || (bias && !aligned(bias, 4)))
+            return CONVROT_EINVAL;
+        const int64_t ye = need_scales ? elem_bytes(y_dtype) : 4;
+        if (!aligned(Y, (uintptr_t)ye))
+            return CONVROT_EINVAL;
+        out->y = rows_span(Y, M, N, ldy, ye);
+        out->qw = span_of(Qw, N * K);
+        out->sw = need_scales ? span_of(s_w, 4 * N) : Span{};
+        out->b = need_scales ? span_of(bias, 4 * N) : Span{};
+    }
+    return CONVROT_OK;
+}
+
+bool y_hits_weights(const LinearCheck &c, const LinearCheck &w)
+{
+    return overlap(c.y, w.qw) || overlap(c.y, w.sw) || overlap(c.y, w.b);
+}
+
+int check_contraction_k(int64_t K)
+{
+    if (K < 1)
+        return CONVROT_EINVAL;
+    if (K % 64 != 0)
+        return CONVROT_EUNSUPPORTED;
+    if (K > kMaxContractionK)
+        return CONVROT_EOVERFLOW;
+    return CONVROT_OK;
+}
+
+GemmLinear make_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t N,
+                       float alpha, void *Y, int kind, int64_t ldy)
+{
+    GemmLinear l;
+    std::memset(&l, 0, sizeof l);
+    l.Qw = Qw;
+    l.s_w = s_w;
+    l.bias = bias;
+    l.Y = Y;
+    l.N = N;
+    l.ldy = ldy;
+    l.alpha = alpha;
+    l.out_kind = kind;
+    const uintptr_t vec_bytes = kind == kOutBF16 ? 8 : 16;
+    l.vec_store = (aligned(Y, vec_bytes) && ldy % 4 == 0) ? 1 : 0;
+    return l;
+}
+
+int out_kind_of(int y_dtype) { return y_dtype == CONVROT_BF16 ? kOutBF16 : kOutF32; }
+
+}  // namespace
+
+extern "C" {
+
+size_t convrot_packed_bytes(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 1)
+        return 0;
+    const int64_t m_pad = round_up(M, 4);
+    return (size_t)(m_pad * K + 4 * m_pad);
+}
+
+size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed)
+{
+    if (n_packed < 0)
+        return 0;
+    return (size_t)n_packed * (size_t)round_up((int64_t)convrot_packed_bytes(M, K), 256);
+}
+
+int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          int group_size, float input_scale, void *packed, void *stream)
+{
+    int rc = check_quantize_args(X, x_dtype, M, K, ldx, group_size, input_scale);
+    if (rc != CONVROT_OK)
+        return rc;
+    if (M == 0)
+        return CONVROT_OK;
+    if (!packed || !aligned(packed, 16))
+        return CONVROT_EINVAL;
+    if (overlap(rows_span(X, M, K, ldx, elem_bytes(x_dtype)),
+                span_of(packed, (int64_t)convrot_packed_bytes(M, K))))
+        return CONVROT_EOVERLAP;
+    (void)hipGetLastError();
+    return hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, input_scale, packed,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+                const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
+                int y_dtype, int64_t ldy, void *stream)
+{
+    if (M < 0)
+        return CONVROT_EINVAL;
+    int rc = check_contraction_k(K);
+    if (rc != CONVROT_OK)
+        return rc;
+    LinearCheck c;
+    rc = check_linear(Qw, s_w, bias, M, K, N, input_scale, Y, y_dtype, ldy, true, &c);
+    if (rc != CONVROT_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return CONVROT_OK;
+    if (!Qx || !s_x || !aligned(Qx, 16) || !aligned(s_x, 4))
+        return CONVROT_EINVAL;
+    if (overlap(c.y, span_of(Qx, M * K)) || overlap(c.y, span_of(s_x, 4 * M)) ||
+        y_hits_weights(c, c))
+        return CONVROT_EOVERLAP;
+    GemmProblem p;
+    std::memset(&p, 0, sizeof p);
+    p.Qx = Qx;
+    p.s_x = s_x;
+    p.M = M;
+    p.K = K;
+    p.n_lin = 1;
+    p.lin[0] = make_linear(Qw, s_w, bias, N, input_scale, Y, out_kind_of(y_dtype), ldy);
+    (void)hipGetLastError();
+    return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
+                          int32_t *A, void *stream)
+{
+    if (M < 0)
+        return CONVROT_EINVAL;
+    int rc = check_contraction_k(K);
+    if (rc != CONVROT_OK)
+        return rc;
+    LinearCheck c;
+    rc = check_linear(Qw, nullptr, nullptr, M, K, N, 1.0f, A, CONVROT_F32, N, false, &c);
+    if (rc != CONVROT_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return CONVROT_OK;
+    if (!Qx || !aligned(Qx, 16))
+        return CONVROT_EINVAL;
+    if (overlap(c.y, span_of(Qx, M * K)) || overlap(c.y, c.qw))
+        return CONVROT_EOVERLAP;
+    GemmProblem p;
+    std::memset(&p, 0, sizeof p);
+    p.Qx = Qx;
+    p.s_x = nullptr;
+    p.M = M;
+    p.K = K;
+    p.n_lin = 1;
+    p.lin[0] = make_linear(Qw, nullptr, nullptr, N, 1.0f, A, kOutI32, N);
+    (void)hipGetLastError();
+    return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               int group_size, int n, const convrot_linear_desc *descs,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n < 1 || n > kMaxLinears || !descs)
+        return CONVROT_EINVAL;
+    int rc = check_quantize_args(X, x_dtype, M, K, ldx, group_size, 1.0f);
+    if (rc != CONVROT_OK)
+        return rc;
+    rc = check_contraction_k(K);
+    if (rc != CONVROT_OK)
+        return rc;
+
+    LinearCheck chk[kMaxLinears];
+    float scales[kMaxLinears];
+    int slot_of[kMaxLinears];
+    int n_slots = 0;
+    for (int i = 0; i < n; ++i) {
+        const convrot_linear_desc &d = descs[i];
+        rc = check_linear(d.Qw, d.s_w, d.bias, M, K, d.N, d.input_scale, d.Y, d.y_dtype, d.ldy,
+                          true, &chk[i]);
+        if (rc != CONVROT_OK)
+            return rc;
+        int s = 0;
+        while (s < n_slots && scales[s] != d.input_scale)
+            ++s;
+        if (s == n_slots)
+            scales[n_slots++] = d.input_scale;
+        slot_of[i] = s;
+    }
+    if (M == 0)
+        return CONVROT_OK;
+
+    const int64_t pb = (int64_t)convrot_packed_bytes(M, K);
+    const int64_t slot_bytes = round_up(pb, 256);
+    if (!workspace || workspace_bytes < convrot_workspace_bytes(M, K, n_slots))
+        return CONVROT_EWORKSPACE;
+    if (!aligned(workspace, 16))
+        return CONVROT_EINVAL;
+    const Span ws = span_of(workspace, slot_bytes * n_slots);
+    const Span xs = rows_span(X, M, K, ldx, elem_bytes(x_dtype));
+    if (overlap(ws, xs))
+        return CONVROT_EOVERLAP;
+    for (int i = 0; i < n; ++i) {
+        if (overlap(chk[i].y, ws) || overlap(chk[i].qw, ws) || overlap(chk[i].sw, ws) ||
+            overlap(chk[i].b, ws))
+            return CONVROT_EOVERLAP;
+        for (int k = 0; k < n; ++k) {
+            if (y_hits_weights(chk[i], chk[k]))
+                return CONVROT_EOVERLAP;
+            if (k != i && overlap(chk[i].y, chk[k].y))
+                return CONVROT_EOVERLAP;
+        }
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int8_t *base = static_cast<int8_t *>(workspace);
+    for (int s = 0; s < n_slots; ++s) {
+        rc = hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, scales[s],
+                                        base + s * slot_bytes, st));
+        if (rc != CONVROT_OK)
+            return rc;
+    }
+    const int64_t m_pad = round_up(M, 4);
+    for (int s = 0; s < n_slots; ++s) {
+        GemmProblem p;
+        std::memset(&p, 0, sizeof p);
+        p.Qx = base + s * slot_bytes;
+        p.s_x = reinterpret_cast<const float *>(base + s * slot_bytes + m_pad * K);
+        p.M = M;
+        p.K = K;
+        for (int i = 0; i < n; ++i) {
+            if (slot_of[i] != s || descs[i].N == 0)
+                continue;
+            const convrot_linear_desc &d = descs[i];
+            p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, d.input_scale, d.Y,
+                                           out_kind_of(d.y_dtype), d.ldy);
+        }
+        if (p.n_lin == 0)
+            continue;
+        rc = hip_status(launch_gemm(p, st));
+        if (rc != CONVROT_OK)
+            return rc;
+    }
+    return CONVROT_OK;
+}
+
+int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        int group_size, float input_scale, const int8_t *Qw, const float *s_w,
+                        const float *bias, int64_t N, void *Y, int y_dtype, int64_t ldy,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    convrot_linear_desc d;
+    d.Qw = Qw;
+    d.s_w = s_w;
+    d.bias = bias;
+    d.N = N;
+    d.input_scale = input_scale;
+    d.Y = Y;
+    d.y_dtype = y_dtype;
+    d.ldy = ldy;
+    return convrot_int8_linear_shared(X, x_dtype, M, K, ldx, group_size, 1, &d, workspace,
+                                      workspace_bytes, stream);
+}
+
+const char *convrot_status_string(int status)
+{
+    switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_EINVAL: return "invalid argument (null pointer, shape, stride, alignment or input scale)";
+    case CONVROT_EUNSUPPORTED: return "unsupported group size, K granularity or dtype";
+    case CONVROT_EOVERFLOW: return "K too large for an exact int32 accumulator";
+    case CONVROT_EOVERLAP: return "an output overlaps a buffer that the same kernel reads";
+    case CONVROT_EWORKSPACE: return "workspace missing or too small";
+    case CONVROT_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

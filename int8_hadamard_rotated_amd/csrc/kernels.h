@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (convrot_api.cpp) and the
+// gfx950 kernels (quantize.hip, gemm_i8.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot_detail {
+
+// ---------------------------------------------------------------- quantize
+// Largest row (in elements) the quantizer handles for a given K: one
+// workgroup per group of rows, at most 256 quads of 4 lanes per row.
+int64_t quantize_max_k(int64_t K);
+
+// Launch the rotate + row-max + quantize + pack kernel.  Arguments are
+// already validated (see convrot_quantize_rows).
+hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                           float alpha, void *packed, hipStream_t stream);
+
+// ------------------------------------------------------------------- GEMM
+constexpr int kMaxLinears = 16;
+
+enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
+
+struct GemmLinear {
+    const int8_t *Qw;    // [N][K]
+    const float *s_w;    // [N] or null
+    const float *bias;   // [N] or null
+    void *Y;             // [M][ldy]
+    int64_t N;
+    int64_t ldy;
+    float alpha;         // divisor; 1 = none
+    int out_kind;        // OutKind
+    int vec_store;       // Y row starts allow 4-element vector stores
+    int tiles_n;         // filled by the launcher
+    int tile_begin;      // filled by the launcher: first linear tile index
+};
+
+struct GemmProblem {
+    const int8_t *Qx;    // [M][K], row stride K
+    const float *s_x;    // [M]
+    int64_t M;
+    int64_t K;
+    int n_lin;
+    GemmLinear lin[kMaxLinears];
+};
+
+// Launch one grouped contraction + reconstruction over all linears of `p`.
+hipError_t launch_gemm(GemmProblem p, hipStream_t stream);
+
+}  // namespace convrot_detail

@@ -1,0 +1,321 @@
+// Rotate + row-max + quantize + pack, one pass over X (gfx950, wave64).
+//
+// Computes, per activation row (page "INT8 Convrot Safetensors", section
+// "How INT8 convrot works", subsection "Runtime activation quantization"):
+//   x  = widen(X[r, :]) * alpha            (multiply only when alpha != 1)
+//   y  = x R_G per contiguous G-group       (R_G = H4^(x)n, G = 4^n)
+//   m  = max |y| over the whole row
+//   s  = fl(m / 127)  and  q = rne(fl(y * fl(127 / m)))  (m = 0: s = 0, q = 0)
+// and writes the packed tensor: int8 [M_pad][K] then float [M_pad]
+// (page "ggml operator extensions", section "sd.cpp integration": rows padded
+// to a multiple of four, followed by the F32 row scales).
+//
+// Every binary32 operation is the oracle's, in the oracle's order: one H4 per
+// base-4 digit of the in-group index, digit 0 first, each as
+// s = (x0 + x1) + (x2 + x3), h = s * 0.5, y_j = h - x_{3-j}.
+//
+// Data layout.  A quad (4 adjacent lanes, j = j0 + 2*j1) owns a span of
+// 32*NC consecutive elements of one row; each lane holds NC chunks of 8
+// consecutive elements (p = 0..7).  Chunk c of lane j starts at span offset
+//   8*j0 + 16*(c & 1) + 32*j1 + 64*(c >> 1)
+// so the element index is e = p + 8*j0 + 16*c0 + 32*j1 + 64*c1, and its
+// base-4 digits sit at
+//   digit 0 = p & 3                      in-register
+//   digit 1 = (p >> 2) + 2*j0            low bit in-register, high bit lane^1
+//   digit 2 = c0 + 2*j1                  low bit in-register, high bit lane^2
+//   digit 3 = c1 & 3                     in-register (G = 256, NC = 8)
+// A digit split as (in-register low bit, lane high bit) keeps the oracle's
+// pairing: each lane forms x_{2H} + x_{2H+1} locally, adds its partner's pair
+// sum through one DPP quad_perm, and IEEE addition being commutative, both
+// lanes hold the bits of (x0 + x1) + (x2 + x3).  Output y_{2H+l} = h - x_{3-2H-l}
+// needs the partner's element with the other low bit: y[l] = h - partner[1-l].
+// No lane-dependent selects are needed, and every DPP exchange stays inside a
+// quad, which is always fully active.
+//
+// One workgroup holds R whole rows (R * quads_per_row quads); the row maximum
+// is reduced in-lane, across the quad (DPP), then across the row's quads with
+// an LDS unsigned max (non-negative binary32 values order like their bits).
+//
+// Codes: t = fl(y * inv) lies in [-127 - 2^-17, 127 + 2^-17] because
+// |y| <= m and inv = fl(127/m), so round-half-even(t) is already within
+// [-127, 127] and the clamp of the formula never changes a value.  The
+// rounding uses fl(t + 1.5 * 2^23): for |t| < 2^22 that sum is exactly
+// 1.5 * 2^23 + rne(t) (ulp 1, and 1.5 * 2^23 is even, so ties go to the even
+// code), whose low byte is the two's-complement int8 code.
+#pragma clang fp contract(off)
+
+#include "kernels.h"
+
+namespace convrot_detail {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kQuadPermXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadPermXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// H4 on four in-register values.
+__device__ __forceinline__ void h4_local(float &x0, float &x1, float &x2, float &x3)
+{
+    const float s = (x0 + x1) + (x2 + x3);
+    const float h = s * 0.5f;
+    const float y0 = h - x3, y1 = h - x2, y2 = h - x1, y3 = h - x0;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+}
+
+// H4 on a digit whose low bit is in-register (lo0: 0, lo1: 1) and whose high
+// bit is the lane bit that CTRL flips.
+template <int CTRL>
+__device__ __forceinline__ void h4_split(float &lo0, float &lo1)
+{
+    const float pair = lo0 + lo1;
+    const float s = pair + quad_swap<CTRL>(pair);
+    const float h = s * 0.5f;
+    const float p0 = quad_swap<CTRL>(lo0);
+    const float p1 = quad_swap<CTRL>(lo1);
+    lo0 = h - p1;
+    lo1 = h - p0;
+}
+
+__device__ __forceinline__ void load8(const float *src, float (&v)[8])
+{
+    const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src));
+    const v4f b = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src) + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// bf16 -> binary32 is exact: the bf16 bits are the upper half.
+__device__ __forceinline__ void load8(const uint16_t *src, float (&v)[8])
+{
+    const v4u u = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src));
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+}
+
+// Low bytes of four words -> one word (byte i from w[i]).
+__device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3)
+{
+    const unsigned lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);
+    const unsigned hi = __builtin_amdgcn_perm(w3, w2, 0x04000c0cu);
+    return lo | hi;
+}
+
+template <typename XT, int G, int NC, bool SCALED>
+__global__ __launch_bounds__(1024) void quantize_rows_kernel(
+    const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
+    int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
+{
+    static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
+    static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    __shared__ unsigned row_max[256];
+
+    const int tid = threadIdx.x;
+    const int quad = tid >> 2;
+    const int j0 = tid & 1, j1 = (tid >> 1) & 1;
+    const int row_local = quad / quads_per_row;
+    const int q_in_row = quad - row_local * quads_per_row;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
+    const int64_t span0 = (int64_t)q_in_row * (32 * NC);
+    // A quad never straddles rows, so this branch is uniform per quad and the
+    // DPP exchanges below only read lanes that take the same path.
+    const bool live = row < M;
+
+    if (tid < rows_per_wg)
+        row_max[tid] = 0u;
+    __syncthreads();
+
+    float v[NC][8];
+    if (live) {
+        const XT *xr = X + row * ldx + span0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            load8(xr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1), v[c]);
+
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    v[c][p] = v[c][p] * alpha;
+        }
+
+        // digit 0 (stride 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
+            h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
+        }
+        // digit 1 (stride 4): low bit p>>2, high bit lane bit 0
+        if constexpr (G >= 16) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    h4_split<kQuadPermXor1>(v[c][p], v[c][p + 4]);
+        }
+        // digit 2 (stride 16): low bit c&1, high bit lane bit 1
+        if constexpr (G >= 64) {
+#pragma unroll
+            for (int c = 0; c < NC; c += 2)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    h4_split<kQuadPermXor2>(v[c][p], v[c + 1][p]);
+        }
+        // digit 3 (stride 64): chunk bits 1..2
+        if constexpr (G >= 256) {
+#pragma unroll
+            for (int c0 = 0; c0 < 2; ++c0)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    h4_local(v[c0][p], v[c0 + 2][p], v[c0 + 4][p], v[c0 + 6][p]);
+        }
+
+        // row max: lane, quad (DPP), then the row's quads (LDS)
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                m = fmaxf(m, fabsf(v[c][p]));
+        m = fmaxf(m, quad_swap<kQuadPermXor1>(m));
+        m = fmaxf(m, quad_swap<kQuadPermXor2>(m));
+        if ((tid & 3) == 0)
+            atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
+    }
+    __syncthreads();
+    if (row >= M_pad)
+        return;
+
+    int8_t *qr = Q + row * K + span0;
+    if (!live) {
+        // pad rows of the packed tensor: zero codes, zero scale
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            *reinterpret_cast<v2u *>(qr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1)) = v2u{0u, 0u};
+        if (q_in_row == 0 && (tid & 3) == 0)
+            S[row] = 0.0f;
+        return;
+    }
+
+    const float m = __builtin_bit_cast(float, row_max[row_local]);
+    const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
+    if (q_in_row == 0 && (tid & 3) == 0)
+        S[row] = __fdiv_rn(m, 127.0f);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        unsigned w[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const float t = v[c][p] * inv;
+            w[p] = __builtin_bit_cast(unsigned, t + 12582912.0f);
+        }
+        v2u out;
+        out.x = pack_low_bytes(w[0], w[1], w[2], w[3]);
+        out.y = pack_low_bytes(w[4], w[5], w[6], w[7]);
+        *reinterpret_cast<v2u *>(qr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1)) = out;
+    }
+}
+
+int gcd_int(int a, int b)
+{
+    while (b) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+template <typename XT, int G, int NC>
+void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, void *packed,
+                  hipStream_t stream)
+{
+    const int64_t m_pad = (M + 3) / 4 * 4;
+    const int qr = (int)(K / (32 * NC));
+    // smallest row count that fills whole waves, then grow towards 256 threads
+    int rows = 16 / gcd_int(qr, 16);
+    if (4 * qr * rows > 1024)
+        rows = 1024 / (4 * qr) > 0 ? 1024 / (4 * qr) : 1;
+    while (4 * qr * rows * 2 <= 256)
+        rows *= 2;
+    const int threads = 4 * qr * rows;
+    const int64_t blocks = (m_pad + rows - 1) / rows;
+    int8_t *Q = static_cast<int8_t *>(packed);
+    float *S = reinterpret_cast<float *>(Q + m_pad * K);
+    if (alpha != 1.0f)
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true>), dim3((unsigned)blocks),
+                           dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
+                           alpha, Q, S, qr, rows);
+    else
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false>), dim3((unsigned)blocks),
+                           dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
+                           alpha, Q, S, qr, rows);
+}
+
+template <typename XT, int NC>
+void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, void *packed,
+               hipStream_t stream)
+{
+    switch (G) {
+    case 4: launch_typed<XT, 4, NC>(X, M, K, ldx, alpha, packed, stream); break;
+    case 16: launch_typed<XT, 16, NC>(X, M, K, ldx, alpha, packed, stream); break;
+    case 64: launch_typed<XT, 64, NC>(X, M, K, ldx, alpha, packed, stream); break;
+    default:
+        if constexpr (NC == 8)
+            launch_typed<XT, 256, 8>(X, M, K, ldx, alpha, packed, stream);
+        break;
+    }
+}
+
+template <typename XT>
+void launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                  void *packed, hipStream_t stream)
+{
+    if (K % 256 == 0)
+        launch_nc<XT, 8>(G, X, M, K, ldx, alpha, packed, stream);
+    else if (K % 128 == 0)
+        launch_nc<XT, 4>(G, X, M, K, ldx, alpha, packed, stream);
+    else
+        launch_nc<XT, 2>(G, X, M, K, ldx, alpha, packed, stream);
+}
+
+}  // namespace
+
+int64_t quantize_max_k(int64_t K)
+{
+    // 256 quads per row at most; a quad covers 256, 128 or 64 elements.
+    if (K % 256 == 0)
+        return 256 * 256;
+    if (K % 128 == 0)
+        return 256 * 128;
+    return 256 * 64;
+}
+
+hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                           float alpha, void *packed, hipStream_t stream)
+{
+    if (x_dtype == 0)
+        launch_dtype<float>(G, X, M, K, ldx, alpha, packed, stream);
+    else
+        launch_dtype<uint16_t>(G, X, M, K, ldx, alpha, packed, stream);
+    return hipGetLastError();
+}
+
+}  // namespace convrot_detail

@@ -1,0 +1,180 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+that include/convrot.h declares, and rejects bad arguments before anything is
+enqueued.  Every call here fails validation (or is a no-op), so no HIP API is
+reached; the pointers are fake, well-aligned addresses that are never touched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int8_hadamard_rotated_amd as cr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+OK, EINVAL, EUNSUP, EOVF, EOVL, EWS = cr.OK, cr.EINVAL, cr.EUNSUPPORTED, cr.EOVERFLOW, cr.EOVERLAP, cr.EWORKSPACE
+BASE = 0x7F00_0000_0000            # fake, 256-byte aligned device addresses
+MB = 1 << 20
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"typedef\s+(enum|struct)\s*\{.*?\}\s*\w+\s*;", "", text, flags=re.S)
+    text = re.sub(r"#[^\n]*", "", text)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}]*\)\s*;", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cr.library()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted([
+        "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
+        "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
+        "convrot_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cr.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, f"{name} not exported with C linkage"
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code in (OK, EINVAL, EUNSUP, EOVF, EOVL, EWS, cr.EHIP):
+        s = cr.convrot_status_string(code)
+        assert s and s != "unknown status"
+    assert cr.convrot_status_string(12345) == "unknown status"
+
+
+def test_size_queries():
+    assert cr.convrot_packed_bytes(5, 256) == 8 * 256 + 4 * 8
+    assert cr.convrot_packed_bytes(4096, 3072) == 4096 * 3072 + 4 * 4096
+    assert cr.convrot_packed_bytes(0, 3072) == 0
+    assert cr.convrot_packed_bytes(-1, 3072) == 0
+    assert cr.convrot_workspace_bytes(5, 256, 1) == 2304      # 2080 rounded up to 256
+    assert cr.convrot_workspace_bytes(5, 256, 2) == 4608
+    assert cr.convrot_workspace_bytes(4096, 3072, 2) == 2 * (4096 * 3072 + 4 * 4096)
+
+
+def q(lib, X=BASE, dt=cr.F32, M=8, K=256, ldx=None, G=16, a=1.0, packed=BASE + 64 * MB):
+    return lib.convrot_quantize_rows(ctypes.c_void_p(X), dt, M, K, K if ldx is None else ldx, G,
+                                     ctypes.c_float(a), ctypes.c_void_p(packed), None)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, G=8) == EUNSUP
+    assert q(lib, G=1) == EUNSUP
+    assert q(lib, G=1024, K=2048) == EUNSUP
+    assert q(lib, K=100, G=4) == EUNSUP                  # K % 64
+    assert q(lib, K=320, G=256) == EUNSUP                # K % G
+    assert q(lib, K=65792, G=256) == EUNSUP              # longer than one workgroup's row
+    assert q(lib, dt=7) == EUNSUP
+    assert q(lib, M=-1) == EINVAL
+    assert q(lib, K=0) == EINVAL
+    assert q(lib, ldx=128) == EINVAL                     # ldx < K
+    assert q(lib, ldx=258) == EINVAL                     # row stride not a 16-byte multiple
+    assert q(lib, X=0) == EINVAL
+    assert q(lib, X=BASE + 4) == EINVAL                  # X misaligned
+    assert q(lib, packed=0) == EINVAL
+    assert q(lib, packed=BASE + 8 + 64 * MB) == EINVAL   # packed misaligned
+    for a in (0.0, -1.0, float("inf"), float("nan")):
+        assert q(lib, a=a) == EINVAL
+    assert q(lib, packed=BASE + 1024) == EOVL            # packed overlaps X
+    assert q(lib, M=0) == OK                             # empty input: nothing enqueued
+    assert q(lib, M=0, X=0, packed=0) == OK
+
+
+def lin(lib, Qx=BASE, sx=BASE + 8 * MB, M=8, K=256, Qw=BASE + 16 * MB, sw=BASE + 24 * MB,
+        b=BASE + 25 * MB, N=32, a=1.0, Y=BASE + 32 * MB, dt=cr.F32, ldy=None):
+    return lib.int8_linear(ctypes.c_void_p(Qx), ctypes.c_void_p(sx), M, K, ctypes.c_void_p(Qw),
+                           ctypes.c_void_p(sw), ctypes.c_void_p(b), N, ctypes.c_float(a),
+                           ctypes.c_void_p(Y), dt, N if ldy is None else ldy, None)
+
+
+def test_int8_linear_validation(lib):
+    assert lin(lib, K=100) == EUNSUP
+    assert lin(lib, K=133184) == EOVF                    # K * 127^2 would exceed int32
+    assert lin(lib, K=0) == EINVAL
+    assert lin(lib, M=-2) == EINVAL
+    assert lin(lib, N=-1) == EINVAL
+    assert lin(lib, ldy=16) == EINVAL
+    assert lin(lib, dt=3) == EUNSUP
+    assert lin(lib, Qx=0) == EINVAL
+    assert lin(lib, sx=0) == EINVAL
+    assert lin(lib, Qw=0) == EINVAL
+    assert lin(lib, Y=0) == EINVAL
+    assert lin(lib, Qw=BASE + 16 * MB + 4) == EINVAL
+    assert lin(lib, Y=BASE + 32 * MB + 2) == EINVAL
+    assert lin(lib, a=0.0) == EINVAL
+    assert lin(lib, Y=BASE + 16 * MB + 256) == EOVL      # Y overlaps Qw
+    assert lin(lib, Y=BASE + 24 * MB) == EOVL            # Y overlaps s_w
+    assert lin(lib, Y=BASE + 8 * MB) == EOVL             # Y overlaps s_x
+    assert lin(lib, Y=BASE) == EOVL                      # Y overlaps Qx
+    assert lin(lib, M=0) == OK
+    assert lin(lib, N=0) == OK
+    # the largest K that is still exact passes the K check (then fails on Qx)
+    assert lin(lib, K=133120, Qx=0) == EINVAL
+
+
+def test_gemm_i32_validation(lib):
+    f = lib.convrot_int8_gemm_i32
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), 4, 133184, 4,
+             ctypes.c_void_p(BASE + 2 * MB), None) == EOVF
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), 4, 96, 4,
+             ctypes.c_void_p(BASE + 2 * MB), None) == EUNSUP
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), 4, 64, 4,
+             ctypes.c_void_p(BASE + MB), None) == EOVL
+    assert f(None, ctypes.c_void_p(BASE + MB), 4, 64, 4, ctypes.c_void_p(BASE + 2 * MB), None) == EINVAL
+    assert f(None, None, 0, 64, 4, None, None) == OK
+
+
+def desc(Qw, Y, N=32, a=1.0, sw=None, b=None, dt=cr.F32):
+    d = cr.LinearDesc()
+    d.Qw, d.Y, d.N, d.input_scale, d.s_w, d.bias, d.y_dtype, d.ldy = Qw, Y, N, a, sw, b, dt, N
+    return d
+
+
+def shared(lib, ds, ws=BASE + 512 * MB, ws_bytes=1 << 30, M=8, K=256, X=BASE, G=16):
+    arr = (cr.LinearDesc * max(len(ds), 1))(*ds)
+    return lib.convrot_int8_linear_shared(ctypes.c_void_p(X), cr.F32, M, K, K, G, len(ds), arr,
+                                          ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_shared_validation(lib):
+    W1, W2 = BASE + 64 * MB, BASE + 96 * MB
+    Y1, Y2 = BASE + 128 * MB, BASE + 160 * MB
+    good = [desc(W1, Y1), desc(W2, Y2, a=0.5)]
+    need = cr.convrot_workspace_bytes(8, 256, 2)
+    assert shared(lib, []) == EINVAL
+    assert shared(lib, [desc(W1, Y1)] * 17) == EINVAL
+    assert shared(lib, good, ws=0) == EWS
+    assert shared(lib, good, ws_bytes=need - 1) == EWS
+    assert shared(lib, [desc(W1, Y1), desc(W2, Y1 + 64)]) == EOVL          # outputs overlap
+    assert shared(lib, [desc(W1, Y1), desc(W2, W1 + 128)]) == EOVL         # output hits a weight
+    assert shared(lib, good, ws=Y1) == EOVL                                 # workspace hits an output
+    assert shared(lib, good, ws=BASE) == EOVL                               # workspace hits X
+    assert shared(lib, [desc(W1, Y1, a=-1.0)]) == EINVAL
+    assert shared(lib, good, G=2) == EUNSUP
+    assert shared(lib, good, M=0) == OK
+
+
+def test_fused_validation(lib):
+    f = lib.convrot_int8_linear
+    args = lambda Y, ws, wsb: (ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, 16, ctypes.c_float(1.0),
+                               ctypes.c_void_p(BASE + 64 * MB), None, None, 32, ctypes.c_void_p(Y),
+                               cr.F32, 32, ctypes.c_void_p(ws), wsb, None)
+    need = cr.convrot_workspace_bytes(8, 256, 1)
+    assert f(*args(BASE + 128 * MB, BASE + 256 * MB, need - 16)) == EWS
+    assert f(*args(BASE + 64 * MB, BASE + 256 * MB, need)) == EOVL          # Y on the weights
+    assert f(*args(BASE + 256 * MB, BASE + 256 * MB, need)) == EOVL         # Y on the workspace

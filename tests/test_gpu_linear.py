@@ -1,0 +1,183 @@
+"""GPU contraction and reconstruction against the CPU oracle.
+
+The int32 accumulator must match bit for bit; Y is checked bit for bit as well
+(the gate the task sets is a max relative error of 1e-5 for fp32 and 1e-2 for
+bf16 outputs; the reported error is printed and asserted against that gate,
+then exactness is asserted on top)."""
+import numpy as np
+import pytest
+
+import int8_hadamard_rotated_amd as cr
+import oracle
+import workloads
+from gpu_util import THREADS, assert_bits_equal, bf16_to_f32, dev, dev_x, host, max_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+F32_GATE, BF16_GATE = 1e-5, 1e-2
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def check_y(got, want, y_dtype, what):
+    if y_dtype == oracle.BF16:
+        err = max_rel_err(bf16_to_f32(got), bf16_to_f32(want))
+        assert err <= BF16_GATE, f"{what}: max rel err {err}"
+    else:
+        err = max_rel_err(got, want)
+        assert err <= F32_GATE, f"{what}: max rel err {err}"
+    assert_bits_equal(got, want, what)
+
+
+GEMM_SHAPES = [(1, 64, 1), (3, 128, 17), (129, 192, 250), (257, 3072, 300), (64, 12288, 96),
+               (4096 + 13, 128, 4096 + 7)]
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_i32_bit_exact(orc, M, K, N):
+    rng = np.random.default_rng(M + K + N)
+    Qx = workloads.random_codes(rng, (M, K))
+    Qw = workloads.random_codes(rng, (N, K))
+    say("gemm_i32", M, K, N)
+    A = host(cr.convrot_int8_gemm_i32(dev(Qx), dev(Qw)))
+    assert_bits_equal(A, orc.gemm_i32(Qx, Qw, threads=THREADS), f"A {M}x{K}x{N}")
+
+
+def test_gemm_i32_extreme_k(orc):
+    """The largest K with an exact int32 result, at the extreme codes."""
+    K = 133120
+    Qx = np.full((4, K), 127, np.int8)
+    Qx[1] = -127
+    Qw = np.full((70, K), 127, np.int8)
+    Qw[3::2] = -127
+    say("gemm_i32 max K")
+    A = host(cr.convrot_int8_gemm_i32(dev(Qx), dev(Qw)))
+    want = orc.gemm_i32(Qx, Qw, threads=THREADS)
+    assert abs(int(want[0, 0])) == K * 127 * 127
+    assert_bits_equal(A, want, "A at max K")
+
+
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+@pytest.mark.parametrize("M,K,N", [(129, 192, 250), (1024 + 3, 256, 4096 + 5)])
+def test_int8_linear_bit_exact(orc, y_dtype, M, K, N):
+    rng = np.random.default_rng(3 * M + N)
+    X = workloads.gaussian_activations(rng, M, K, 0.01, 30.0, workloads.F32)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    G = 64
+    Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+    for alpha in (1.0, 0.5, 0.3):
+        p = orc.quantize_rows(X, G, alpha, threads=THREADS)
+        A = orc.gemm_i32(p.q, Qw, threads=THREADS)
+        Qx_d, sx_d, Qw_d, sw_d, b_d = dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b)
+        for use_sw, use_b in ((True, True), (False, True), (True, False), (False, False)):
+            say("int8_linear", M, K, N, y_dtype, alpha, use_sw, use_b)
+            want = orc.epilogue(A, p.s, sw if use_sw else None, b if use_b else None, alpha,
+                                y_dtype, threads=THREADS)
+            Y = cr.int8_linear(Qx_d, sx_d, Qw_d, sw_d if use_sw else None, b_d if use_b else None,
+                               alpha, y_dtype=y_dtype)
+            check_y(host(Y), want, y_dtype, f"Y {M}x{K}x{N} a={alpha} sw={use_sw} b={use_b}")
+
+
+def test_int8_linear_strided_output(orc):
+    """ldy > N, and an output whose rows do not allow vector stores."""
+    rng = np.random.default_rng(5)
+    import torch
+    M, K, N = 70, 256, 61
+    Qx = workloads.random_codes(rng, (M, K))
+    Qw = workloads.random_codes(rng, (N, K))
+    sx = workloads.random_scales(rng, M)
+    sw = workloads.random_scales(rng, N)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    want = orc.epilogue(orc.gemm_i32(Qx, Qw), sx, sw, b)
+    for ld in (N, 64, 67):
+        big = torch.full((M, ld), -7.0, dtype=torch.float32, device="cuda:0")
+        Y = big[:, :N]
+        say("strided Y", ld)
+        cr.int8_linear(dev(Qx), dev(sx), dev(Qw), dev(sw), dev(b), 1.0, Y=Y)
+        got = host(big)
+        assert_bits_equal(np.ascontiguousarray(got[:, :N]), want, f"Y ldy={ld}")
+        assert np.all(got[:, N:] == -7.0), "wrote past N"
+
+
+def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    rows |= {0, M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["tiny", "attn", "mlp_up", "mlp_down"])
+def test_fused_workload(orc, name):
+    """The fused entry at each workload's full size, in the configuration the
+    benchmark runs; Y compared in full where the oracle is quick, else on
+    sampled rows (each row of the layer is independent of the others)."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    Qw, sw = orc.weight_prep(inp.W[0], w.G, threads=THREADS)
+    yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
+    say("fused", name)
+    Y = host(cr.convrot_int8_linear(dev_x(inp.X), w.G, 1.0, dev(Qw), dev(sw), dev(inp.b[0]),
+                                    y_dtype=yd))
+    rows = np.arange(w.M) if w.M * w.N * w.K <= 2 ** 34 else sample_rows(w.M, 24, w.seed)
+    want = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[0], 1.0, yd, threads=THREADS)
+    check_y(np.ascontiguousarray(Y[rows]), want, yd, f"{name} Y")
+
+
+def test_shared_qkv(orc):
+    """Three linears sharing one packed input plus one at input scale 0.5:
+    each output against the oracle, against separate fused calls, and the
+    0.5 linear against the same weights at scale 1 (bit-identical, since
+    multiplying by 2^-1 before the rotation and dividing after are exact)."""
+    w = workloads.WORKLOADS["qkv"]
+    inp = workloads.make_inputs(w)
+    Xd = dev_x(inp.X)
+    preps = [orc.weight_prep(W, w.G, threads=THREADS) for W in inp.W]
+    lins = [dict(Qw=dev(q), s_w=dev(s), bias=dev(b), input_scale=a)
+            for (q, s), b, a in zip(preps, inp.b, w.input_scales)]
+    say("shared qkv")
+    outs = [host(y) for y in cr.convrot_int8_linear_shared(Xd, w.G, lins)]
+    rows = sample_rows(w.M, 16, 33)
+    for j, (y, a) in enumerate(zip(outs, w.input_scales)):
+        Qw, sw = preps[j]
+        want = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[j], a, threads=THREADS)
+        check_y(np.ascontiguousarray(y[rows]), want, oracle.F32, f"qkv linear {j}")
+        say("separate", j)
+        sep = host(cr.convrot_int8_linear(Xd, w.G, a, lins[j]["Qw"], lins[j]["s_w"],
+                                          lins[j]["bias"]))
+        assert_bits_equal(y, sep, f"shared vs separate, linear {j}")
+    say("alpha 0.5 vs 1")
+    one = host(cr.convrot_int8_linear(Xd, w.G, 1.0, lins[3]["Qw"], lins[3]["s_w"],
+                                      lins[3]["bias"]))
+    assert_bits_equal(outs[3], one, "input scale 0.5 vs 1")
+
+
+def test_fused_output_may_alias_input(orc):
+    import torch
+    rng = np.random.default_rng(12)
+    M, K, N = 40, 512, 256
+    X = workloads.gaussian_activations(rng, M, K, 0.01, 20.0, workloads.F32)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    Qw, sw = orc.weight_prep(W, 64)
+    want = orc.linear(X, 64, Qw, sw, b)
+    Xd = dev_x(X)
+    Y = Xd[:, :N]                 # Y overwrites X's storage (row stride K)
+    say("alias")
+    cr.convrot_int8_linear(Xd, 64, 1.0, dev(Qw), dev(sw), dev(b), Y=Y)
+    assert_bits_equal(np.ascontiguousarray(host(Xd)[:, :N]), want, "aliased Y")
+
+
+def test_empty_shapes(orc):
+    import torch
+    Qw = torch.zeros((0, 256), dtype=torch.int8, device="cuda:0")
+    Qx = torch.zeros((5, 256), dtype=torch.int8, device="cuda:0")
+    sx = torch.ones(5, dtype=torch.float32, device="cuda:0")
+    say("empty N")
+    Y = cr.int8_linear(Qx, sx, Qw)
+    assert Y.shape == (5, 0)
+    X = torch.zeros((0, 256), dtype=torch.float32, device="cuda:0")
+    say("empty M")
+    Y = cr.convrot_int8_linear(X, 16, 1.0, torch.zeros((8, 256), dtype=torch.int8, device="cuda:0"))
+    assert Y.shape == (0, 8)

@@ -1,0 +1,107 @@
+"""GPU rotate + quantize + pack against the CPU oracle: the whole packed tensor
+(codes, pad rows, scale tail) must be identical byte for byte."""
+import numpy as np
+import pytest
+
+import int8_hadamard_rotated_amd as cr
+import oracle
+import pins
+import workloads
+from gpu_util import THREADS, assert_bits_equal, dev_x, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def gpu_packed(X: np.ndarray, G: int, alpha: float = 1.0, K=None):
+    Xd = dev_x(X)
+    return host(cr.convrot_quantize_rows(Xd, G, alpha, K=K))
+
+
+@pytest.mark.parametrize("name", ["tiny", "attn", "mlp_up", "qkv", "mlp_down"])
+def test_workload_packed_bit_exact(orc, name):
+    w = workloads.WORKLOADS[name]
+    rng = np.random.default_rng(w.seed)
+    X = workloads.gaussian_activations(rng, w.M, w.K, w.outlier_p, w.outlier_f, w.x_dtype)
+    for alpha in sorted(set(w.input_scales)):
+        say(name, w.M, w.K, w.G, w.x_dtype, "alpha", alpha)
+        want = orc.quantize_rows(X, w.G, alpha, threads=THREADS).raw
+        got = gpu_packed(X, w.G, alpha)
+        assert_bits_equal(got, want, f"{name} packed (alpha={alpha})")
+
+
+EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (129, 3072), (7, 12288),
+               (2, 65536)]
+
+
+@pytest.mark.parametrize("G", [4, 16, 64, 256])
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.BF16])
+def test_edge_shapes(orc, G, dtype):
+    rng = np.random.default_rng(100 + G)
+    for (M, K) in EDGE_SHAPES:
+        if K % G:
+            continue
+        X = workloads.gaussian_activations(rng, M, K, 0.01, 30.0, dtype)
+        for alpha in (1.0, 0.5, 0.3):
+            say("edge", M, K, G, dtype, alpha)
+            assert_bits_equal(gpu_packed(X, G, alpha), orc.quantize_rows(X, G, alpha).raw,
+                              f"M={M} K={K} G={G} {dtype} alpha={alpha}")
+
+
+def test_row_stride(orc):
+    rng = np.random.default_rng(7)
+    for dtype in (workloads.F32, workloads.BF16):
+        wide = workloads.gaussian_activations(rng, 37, 3072 + 64, 0.005, 30.0, dtype)
+        say("ldx", dtype)
+        got = gpu_packed(wide, 256, K=3072)
+        want = orc.quantize_rows(wide, 256, K=3072).raw
+        assert_bits_equal(got, want, f"strided rows {dtype}")
+
+
+def test_special_rows(orc):
+    """Zero rows, the constructed rounding-tie row, constant rows, magnitudes
+    near the contract's limits and a single isolated outlier."""
+    vals, codes = pins.load_tie_row()
+    tie = np.repeat(vals, 16).astype(np.float32)
+    rng = np.random.default_rng(8)
+    K = 256
+    rows = [np.zeros(K, np.float32), tie, np.full(K, 3.25, np.float32),
+            (rng.standard_normal(K) * 2.0 ** 90).astype(np.float32),
+            (rng.standard_normal(K) * 2.0 ** -90).astype(np.float32),
+            np.where(np.arange(K) == 77, 1000.0, 0.0).astype(np.float32),
+            -tie]
+    X = np.stack(rows)
+    for G in (4, 16, 64, 256):
+        for alpha in (1.0, 0.5):
+            say("special rows", G, alpha)
+            got = gpu_packed(X, G, alpha)
+            want = orc.quantize_rows(X, G, alpha).raw
+            assert_bits_equal(got, want, f"special rows G={G} alpha={alpha}")
+    # the tie row itself against the golden codes (G = 16 leaves it unrotated)
+    p = oracle.Packed(gpu_packed(X, 16), X.shape[0], K)
+    assert np.array_equal(p.q[1], np.repeat(codes, 16))
+    assert p.s[1] == np.float32(1.0) and p.s[0] == 0 and np.all(p.q[0] == 0)
+
+
+def test_weight_prep_on_gpu(orc):
+    """The offline weight quantization is the same quantizer on W's rows."""
+    w = workloads.WORKLOADS["attn"]
+    rng = np.random.default_rng(9)
+    W, _ = workloads.gaussian_weights(rng, 3072, 3072)
+    say("weight prep")
+    Qw, sw = orc.weight_prep(W, 256, threads=THREADS)
+    p = oracle.Packed(gpu_packed(W, 256), 3072, 3072)
+    assert_bits_equal(p.q, Qw, "Q_w")
+    assert_bits_equal(p.s, sw, "s_w")
+
+
+def test_empty_rows_enqueue_nothing():
+    import torch
+    X = torch.empty((0, 256), dtype=torch.float32, device="cuda:0")
+    say("empty")
+    out = cr.convrot_quantize_rows(X, 16)
+    assert out.numel() == 0
