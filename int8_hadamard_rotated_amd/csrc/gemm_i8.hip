@@ -13,9 +13,9 @@
 // Both operands are K-contiguous.  A workgroup of 4 waves computes a BM x BN
 // tile; waves form a 2 x 2 grid, each owning (BM/2) x (BN/2) as 16 x 16 MFMA
 // blocks (v_mfma_i32_16x16x64_i8, 64 K-bytes per instruction).  K advances in
-// BK-byte steps through two LDS buffers: the next step's global loads are in
-// flight while the current step's MFMAs run.  LDS rows are padded by 16 bytes
-// so that the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+// 64-byte steps through two LDS buffers, with global loads staged in registers
+// two steps ahead.  The four 16-byte K chunks of each LDS row are XOR-swizzled
+// by row so that the fragment reads of consecutive rows hit distinct banks.
 //
 // The integer sum is exact whatever the order of K, so the lane-to-K mapping
 // inside an MFMA only has to agree between the two operands, which are read
@@ -34,10 +34,13 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 
 template <int BM, int BN, int BK>
 struct Tile {
@@ -45,28 +48,69 @@ struct Tile {
     static constexpr int kWaveN = BN / 2;
     static constexpr int kTM = kWaveM / 16;
     static constexpr int kTN = kWaveN / 16;
-    static constexpr int kStride = BK + 16;               // LDS bytes per row
+    static constexpr int kStride = BK;                    // LDS bytes per row (swizzled)
     static constexpr int kChunksPerRow = BK / 16;
     static constexpr int kAChunks = BM * kChunksPerRow / kThreads;
     static constexpr int kBChunks = BN * kChunksPerRow / kThreads;
     static constexpr int kStageBytes = (BM + BN) * kStride;
+    static constexpr int kStages = 4;                      // LDS ring depth
+    static constexpr int kLoads = (BM + BN) / 64;          // DMA loads per wave per step
+    static constexpr int kScaleOff = kStages * kStageBytes;  // s_x [BM], s_w [BN], bias [BN]
+    static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 2 * BN);
     static_assert(BM * kChunksPerRow % kThreads == 0 && BN * kChunksPerRow % kThreads == 0, "");
-    static_assert(BK % 64 == 0, "");
+    static_assert(BK == 64, "one 16x16x64 MFMA K-step per LDS stage; the swizzle assumes 4 chunks");
 };
 
-__device__ __forceinline__ uint16_t bf16_rne(float t)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, 32-bit data format) over [base, base + bytes).
+__device__ __forceinline__ v4u buffer_rsrc(const int8_t *base, uint32_t bytes)
 {
-    unsigned u = __builtin_bit_cast(unsigned, t);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferFlags};
 }
 
-template <int BM, int BN, int BK>
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.
+// Issued as inline assembly so that the compiler does not serialize its LDS
+// reads behind these loads; the matching waits are explicit (wait_vmcnt).
+__device__ __forceinline__ void dma_x4(v4u rsrc, int voff, int soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
+
+// 4 bytes per lane from buffer offset voff + soff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma_x1(v4u rsrc, int voff, int soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// XOR swizzle of the four 16-byte K chunks of an LDS row.  The fragment read
+// of one MFMA block has lane l read row l%16, chunk l/16; with chunk slot
+// c ^ ((r >> 1) & 3) that read pattern measures free of LDS bank conflicts on
+// gfx950 (SQ_LDS_BANK_CONFLICT = 0), unlike unswizzled, row-padded or
+// low-bit-XOR layouts, which cost two LDS passes per read.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+
+template <int BM, int BN, int BK, bool DIV>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int tiles_m,
                                                               int total_tiles)
 {
     using T = Tile<BM, BN, BK>;
-    __shared__ __attribute__((aligned(16))) int8_t lds[2 * T::kStageBytes];
+    __shared__ __attribute__((aligned(16))) int8_t lds[T::kLdsBytes];
 
     // ---- tile assignment: contiguous tile range per XCD, then group-M order
     const int bid = blockIdx.x;
@@ -90,45 +134,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- global -> LDS chunk assignment (16 bytes per chunk)
-    const int8_t *a_src[T::kAChunks];
-    int a_dst[T::kAChunks];
-#pragma unroll
-    for (int i = 0; i < T::kAChunks; ++i) {
-        const int c = tid + kThreads * i;
-        const int r = c / T::kChunksPerRow, kc = c % T::kChunksPerRow;
-        const int64_t gr = (m0 + r < M) ? m0 + r : M - 1;   // clamped; rows >= M are not stored
-        a_src[i] = p.Qx + gr * K + 16 * kc;
-        a_dst[i] = r * T::kStride + 16 * kc;
-    }
-    const int8_t *b_src[T::kBChunks];
-    int b_dst[T::kBChunks];
-#pragma unroll
-    for (int i = 0; i < T::kBChunks; ++i) {
-        const int c = tid + kThreads * i;
-        const int r = c / T::kChunksPerRow, kc = c % T::kChunksPerRow;
-        const int64_t gr = (n0 + r < N) ? n0 + r : N - 1;
-        b_src[i] = L.Qw + gr * K + 16 * kc;
-        b_dst[i] = BM * T::kStride + r * T::kStride + 16 * kc;
-    }
+    // ---- global -> LDS by direct buffer loads (buffer_load_dwordx4 ... lds):
+    // lane L of a wave writes LDS bytes [M0 + 16 L, M0 + 16 L + 16).  One
+    // instruction of wave w fills the 1 KB of rows 64 i + 16 w .. +16 of an
+    // operand tile; the lane's slot (row L/4, slot L%4) receives logical chunk
+    // (L%4) ^ swz(row), so the rows' 16-byte K chunks are XOR-swizzled and the
+    // fragment reads of consecutive rows hit distinct bank groups.  swz(row)
+    // only depends on row bits 1..2, that is on L/4.
+    //
+    // Each operand tile is addressed through a buffer descriptor that starts
+    // at the tile's first row and ends after its last valid row; rows past M
+    // (or N) fall outside it and are never stored.
+    //
+    // kStages LDS stages form a ring: step ks lives in stage ks % kStages and
+    // its loads are issued kStages - 1 steps ahead.  Before step ks a wave
+    // waits until its own loads for ks have landed (vmcnt), then the barrier
+    // makes every wave's loads visible and also guarantees that every wave is
+    // done with step ks - 1, whose stage the loads for ks + kStages - 1 reuse.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int64_t a_rows = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t b_rows = (N - n0) < BN ? (N - n0) : BN;
+    const v4u a_rsrc = buffer_rsrc(p.Qx + m0 * K, (uint32_t)(a_rows * K));
+    const v4u b_rsrc = buffer_rsrc(L.Qw + n0 * K, (uint32_t)(b_rows * K));
+    const int ld_row = lane >> 2;
+    const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t *)lds;
 
-    v4i ra[T::kAChunks], rb[T::kBChunks];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < T::kAChunks; ++i)
-            ra[i] = *reinterpret_cast<const v4i *>(a_src[i] + k0);
-#pragma unroll
-        for (int i = 0; i < T::kBChunks; ++i)
-            rb[i] = *reinterpret_cast<const v4i *>(b_src[i] + k0);
+    // load q (< kLoads) of a K-step: A rows for q < BM/64, else B rows
+    auto issue_one = [&](int64_t step, int q) {
+        const uint32_t st = lds_base + (uint32_t)(step % T::kStages) * T::kStageBytes;
+        const int k0 = (int)(step * BK);
+        if (q < BM / 64) {
+            dma_x4(a_rsrc, ld_voff, (64 * q + 16 * wave_u) * (int)K + k0,
+                   st + (64 * q + 16 * wave_u) * T::kStride);
+        } else {
+            const int qb = q - BM / 64;
+            dma_x4(b_rsrc, ld_voff, (64 * qb + 16 * wave_u) * (int)K + k0,
+                   st + BM * T::kStride + (64 * qb + 16 * wave_u) * T::kStride);
+        }
     };
-    auto swrite = [&](int buf) {
-        int8_t *base = lds + buf * T::kStageBytes;
+    auto issue = [&](int64_t step) {
 #pragma unroll
-        for (int i = 0; i < T::kAChunks; ++i)
-            *reinterpret_cast<v4i *>(base + a_dst[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < T::kBChunks; ++i)
-            *reinterpret_cast<v4i *>(base + b_dst[i]) = rb[i];
+        for (int q = 0; q < T::kLoads; ++q)
+            issue_one(step, q);
     };
 
     v4i acc[T::kTM][T::kTN];
@@ -138,76 +186,141 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
         for (int j = 0; j < T::kTN; ++j)
             acc[i][j] = v4i{0, 0, 0, 0};
 
-    // fragment read offsets: lane -> (row within 16, 16-byte K slice)
-    const int frag_row = lane & 15, frag_k = 16 * (lane >> 4);
-    const int a_frag = (wm * T::kWaveM + frag_row) * T::kStride + frag_k;
-    const int b_frag = BM * T::kStride + (wn * T::kWaveN + frag_row) * T::kStride + frag_k;
+    // fragment reads: lane -> (row lane%16 of a 16-row block, logical chunk
+    // lane/16); the swizzle of rows 16*i + lane%16 does not depend on i.
+    const int frag_row = lane & 15, frag_chunk = lane >> 4;
+    const int frag_slot = 16 * (frag_chunk ^ swz(frag_row));
+    const int a_frag0 = (wm * T::kWaveM + frag_row) * T::kStride + frag_slot;
+    const int b_frag0 = BM * T::kStride + (wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
 
-    const int64_t ksteps = K / BK;
-    gload(0);
-    swrite(0);
-    __syncthreads();
-    for (int64_t ks = 0; ks < ksteps; ++ks) {
-        const int buf = (int)(ks & 1);
-        if (ks + 1 < ksteps)
-            gload((ks + 1) * BK);
-        const int8_t *base = lds + buf * T::kStageBytes;
+    // ---- main loop.  One K-step: every fragment read is issued first (A
+    // block 0 and the B blocks lead, so the first MFMA waits for two reads
+    // only), then the MFMAs run as kTM groups, one per A block.  When `next`
+    // is a valid step its kLoads DMA loads are spread over the first groups
+    // so that the vector-memory queue drains while the matrix cores work.
+    static_assert(T::kLoads <= T::kTM, "at most one load per MFMA group");
+    auto step_body = [&](int stage, int64_t next) {
+        const int8_t *base = lds + stage * T::kStageBytes;
+        v4i fa[T::kTM], fb[T::kTN];
+        fa[0] = *reinterpret_cast<const v4i *>(base + a_frag0);
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 64) {
-            v4i fa[T::kTM], fb[T::kTN];
+        for (int j = 0; j < T::kTN; ++j)
+            fb[j] = *reinterpret_cast<const v4i *>(base + b_frag0 + j * 16 * T::kStride);
 #pragma unroll
-            for (int i = 0; i < T::kTM; ++i)
-                fa[i] = *reinterpret_cast<const v4i *>(base + a_frag + i * 16 * T::kStride + kk);
+        for (int i = 1; i < T::kTM; ++i)
+            fa[i] = *reinterpret_cast<const v4i *>(base + a_frag0 + i * 16 * T::kStride);
+#pragma unroll
+        for (int i = 0; i < T::kTM; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (next >= 0 && i < T::kLoads)
+                issue_one(next, i);
 #pragma unroll
             for (int j = 0; j < T::kTN; ++j)
-                fb[j] = *reinterpret_cast<const v4i *>(base + b_frag + j * 16 * T::kStride + kk);
-#pragma unroll
-            for (int i = 0; i < T::kTM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (ks + 1 < ksteps)
-            swrite(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The epilogue's row scales, weight scales and bias go to LDS first, by
+    // the same DMA path (64 floats per instruction), so that their latency is
+    // hidden behind the whole main loop.  They are older than every operand
+    // load, so the first operand wait also covers them.
+    const bool want_sx = L.out_kind != kOutI32;
+    const bool has_sw = L.s_w != nullptr, has_bias = L.bias != nullptr;
+    {
+        constexpr int kSeg = (BM + 2 * BN) / 64;        // 64-float segments
+        const v4u sx_rsrc = buffer_rsrc(reinterpret_cast<const int8_t *>(p.s_x + (want_sx ? m0 : 0)),
+                                        want_sx ? (uint32_t)(a_rows * 4) : 0u);
+        const v4u sw_rsrc = buffer_rsrc(reinterpret_cast<const int8_t *>(L.s_w + (has_sw ? n0 : 0)),
+                                        has_sw ? (uint32_t)(b_rows * 4) : 0u);
+        const v4u b_rsrc2 = buffer_rsrc(reinterpret_cast<const int8_t *>(L.bias + (has_bias ? n0 : 0)),
+                                        has_bias ? (uint32_t)(b_rows * 4) : 0u);
+#pragma unroll
+        for (int q = 0; q < kSeg; ++q) {
+            if (q % 4 != wave_u)
+                continue;
+            const uint32_t dst = lds_base + T::kScaleOff + 256 * q;
+            if (q < BM / 64) {
+                if (want_sx)
+                    dma_x1(sx_rsrc, 4 * lane, 256 * q, dst);
+            } else if (q < (BM + BN) / 64) {
+                if (has_sw)
+                    dma_x1(sw_rsrc, 4 * lane, 256 * (q - BM / 64), dst);
+            } else if (has_bias) {
+                dma_x1(b_rsrc2, 4 * lane, 256 * (q - (BM + BN) / 64), dst);
+            }
+        }
     }
 
-    // ---- epilogue.  The MFMA 16x16 result block gives lane l column l%16
-    // and rows 4*(l/16) + v.  Each wave stages one 16-row slice of its
-    // accumulators in LDS (the operand buffers are free by now), then reads it
-    // back four consecutive columns per lane, so that the reconstruction and
-    // the stores work on 4-wide rows (one 16- or 8-byte store per lane).
+    const int64_t ksteps = K / BK;
+#pragma unroll
+    for (int s0 = 0; s0 < T::kStages - 1; ++s0)
+        if (s0 < ksteps)
+            issue(s0);
+    for (int64_t ks = 0; ks < ksteps; ++ks) {
+        // loads issued after step ks's: those of steps ks+1 .. min(ks+kStages-2, last)
+        const int64_t last = ksteps - 1 < ks + T::kStages - 2 ? ksteps - 1 : ks + T::kStages - 2;
+        const int64_t later = last - ks;
+        if (later >= 2)
+            wait_vmcnt<2 * T::kLoads>();
+        else if (later == 1)
+            wait_vmcnt<T::kLoads>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        const int64_t next = ks + T::kStages - 1;
+        step_body((int)(ks % T::kStages), next < ksteps ? next : -1);
+    }
+    __syncthreads();
+
+    // ---- epilogue.  The MFMA 16x16 result block leaves lane l with column
+    // l%16 and rows 4*(l/16) + v.  Each wave stages one 16-row slice of its
+    // accumulators in its own LDS region (the operand ring is free by now),
+    // then reads it back four consecutive columns per lane: slot s of a slice
+    // is (row s / kColQuads, column quad s % kColQuads), and lane l owns slots
+    // l + 64 k.  Half a wave then covers a full 128-column row, so every store
+    // instruction writes whole row segments (256 contiguous bytes for bf16),
+    // the pattern the memory system absorbs at full rate.  The staging region
+    // is private to the wave and LDS operations of one wave complete in
+    // order, so no barrier is needed between writing and reading it.
     constexpr int kStageStride = T::kWaveN + 4;                 // int32 per staged row
     constexpr int kColQuads = T::kWaveN / 4;
     constexpr int kSlots = 16 * kColQuads / 64;
-    static_assert(4 * 16 * kStageStride * 4 <= 2 * T::kStageBytes, "staging fits in LDS");
+    constexpr int kRowStep = 64 / kColQuads;
+    static_assert(64 % kColQuads == 0, "");
+    static_assert(4 * 16 * kStageStride * 4 <= T::kScaleOff, "staging fits in the ring");
     int32_t *stage = reinterpret_cast<int32_t *>(lds) + wave * 16 * kStageStride;
+    const float *sx_lds = reinterpret_cast<const float *>(lds + T::kScaleOff);
+    const float *sw_lds = sx_lds + BM;
+    const float *b_lds = sw_lds + BN;
     const int kind = L.out_kind;
-    const float alpha = L.alpha;
-    const float *s_w = L.s_w;
-    const float *bias = L.bias;
     void *Yv = L.Y;
     const int64_t ldy = L.ldy;
-    const bool vec = L.vec_store != 0;
+    const float alpha = L.alpha;
     const int row_in = 4 * (lane >> 4), col_in = lane & 15;
+    const int cq = lane % kColQuads, rr0 = lane / kColQuads;
+    const int cl = wn * T::kWaveN + 4 * cq;                     // column within the tile
+    const int64_t o = n0 + cl;
+    const bool col_any = o < N;
+    const bool full = (L.vec_store != 0) && (o + 4 <= N);
+    const v4f sw = has_sw ? *reinterpret_cast<const v4f *>(sw_lds + cl) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+    const v4f bo = has_bias ? *reinterpret_cast<const v4f *>(b_lds + cl) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
-        __syncthreads();
+#pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
-            const int slot = lane + 64 * sl;
-            const int rr = slot / kColQuads, cq = slot % kColQuads;
+            const int rr = rr0 + kRowStep * sl;
             const v4i a = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cq);
-            const int64_t r = m0 + wm * T::kWaveM + i * 16 + rr;
-            const int64_t o = n0 + wn * T::kWaveN + 4 * cq;
-            if (r >= M || o >= N)
+            const int rl = wm * T::kWaveM + i * 16 + rr;        // row within the tile
+            const int64_t r = m0 + rl;
+            if (r >= M || !col_any)
                 continue;
-            const bool full = vec && (o + 4 <= N);
             if (kind == kOutI32) {
                 int32_t *y = static_cast<int32_t *>(Yv) + r * ldy + o;
                 if (full) {
@@ -218,19 +331,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
                 }
                 continue;
             }
-            const float sx = p.s_x[r];
+            const float sxr = sx_lds[rl];
             float t[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t oe = (o + e < N) ? o + e : N - 1;
                 float x = (float)a[e];
-                x = x * sx;
-                if (s_w)
-                    x = x * s_w[oe];
-                if (alpha != 1.0f)
+                x = x * sxr;
+                if (has_sw)
+                    x = x * sw[e];
+                if constexpr (DIV)
                     x = __fdiv_rn(x, alpha);
-                if (bias)
-                    x = x + bias[oe];
+                if (has_bias)
+                    x = x + bo[e];
                 t[e] = x;
             }
             if (kind == kOutF32) {
@@ -242,18 +354,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
                         y[e] = t[e];
                 }
             } else {
+                // round to nearest even (the hardware conversion; finite inputs)
+                // Both halves are taken from the packed words with integer
+                // operations (element extraction from a bf16 vector is
+                // miscompiled for the high half by this toolchain).
+                const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
+                const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
                 uint16_t *y = static_cast<uint16_t *>(Yv) + r * ldy + o;
-                const uint16_t h0 = bf16_rne(t[0]), h1 = bf16_rne(t[1]);
-                const uint16_t h2 = bf16_rne(t[2]), h3 = bf16_rne(t[3]);
                 if (full) {
-                    v2u w;
-                    w.x = (unsigned)h0 | ((unsigned)h1 << 16);
-                    w.y = (unsigned)h2 | ((unsigned)h3 << 16);
-                    *reinterpret_cast<v2u *>(y) = w;
+                    *reinterpret_cast<v2u *>(y) = v2u{w0, w1};
                 } else {
-                    const uint16_t hs[4] = {h0, h1, h2, h3};
+                    const unsigned ws[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
                     for (int e = 0; e < 4 && o + e < N; ++e)
-                        y[e] = hs[e];
+                        y[e] = (uint16_t)ws[e];
                 }
             }
         }
@@ -272,8 +385,16 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     }
     if (total == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK>), dim3(total), dim3(kThreads), 0, stream, p,
-                       tiles_m, total);
+    // the unscale division is compiled in only when some linear needs it
+    bool div = false;
+    for (int d = 0; d < p.n_lin; ++d)
+        div = div || p.lin[d].alpha != 1.0f;
+    if (div)
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, true>), dim3(total), dim3(kThreads), 0,
+                           stream, p, tiles_m, total);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, false>), dim3(total), dim3(kThreads), 0,
+                           stream, p, tiles_m, total);
     return hipGetLastError();
 }
 

@@ -181,3 +181,21 @@ def test_empty_shapes(orc):
     say("empty M")
     Y = cr.convrot_int8_linear(X, 16, 1.0, torch.zeros((8, 256), dtype=torch.int8, device="cuda:0"))
     assert Y.shape == (0, 8)
+
+
+def test_bf16_output_subnormal_range(orc):
+    """Outputs around the binary32 / bf16 subnormal boundary: the kernel's bf16
+    conversion must round exactly like the oracle's (nearest, ties to even)."""
+    rng = np.random.default_rng(31)
+    M, K, N = 64, 256, 96
+    Qx = workloads.random_codes(rng, (M, K))
+    Qw = workloads.random_codes(rng, (N, K))
+    A = orc.gemm_i32(Qx, Qw)
+    for sx_scale in (1e-36, 1e-39, 1e-41, 3e-43):
+        sx = (workloads.random_scales(rng, M, 0.5, 2.0) * np.float32(sx_scale)).astype(np.float32)
+        sw = workloads.random_scales(rng, N, 1e-3, 1e-1)
+        for y_dtype in (oracle.F32, oracle.BF16):
+            say("subnormal outputs", sx_scale, y_dtype)
+            want = orc.epilogue(A, sx, sw, None, 1.0, y_dtype)
+            got = host(cr.int8_linear(dev(Qx), dev(sx), dev(Qw), dev(sw), None, 1.0, y_dtype=y_dtype))
+            assert_bits_equal(got, want, f"subnormal-range Y scale={sx_scale} dtype={y_dtype}")
