@@ -5,9 +5,10 @@ One step is one pass of the whole hot path over one batch: the rotate +
 row-max + quantize + pack kernel over X, then the INT8 MFMA contraction with
 the fused reconstruction (scale, weight scale, unscale, bias, output cast).
 These are the two launches the fused entry convrot_int8_linear makes; the
-benchmark issues them as convrot_quantize_rows + int8_linear so that HIP
-events between them time each kernel over the timed region.  For the shared
-QKV workload a step is one convrot_int8_linear_shared call.
+benchmark issues them as convrot_quantize_rows + int8_linear, the same
+kernels.  For the shared QKV workload a step is one convrot_int8_linear_shared
+call.  After the timed steps each kernel is timed on its own (K back-to-back
+launches between two HIP events) for the roofline figures.
 
 Inputs are seeded synthetic DiT-shaped tensors (workloads.py), resident in
 HBM before timing starts.  Several input sets are rotated across steps so that
@@ -74,6 +75,64 @@ def measured_traffic(kind: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean per-dispatch value (KiB) of one counter, by kernel kind."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            kind = ("gemm" if "gemm_i8_kernel" in name else
+                    "quantize" if "quantize_rows_kernel" in name else
+                    "copy" if "elementwise" in name and "neg" in name else None)
+            if kind is not None:
+                vals.setdefault((kind, name), []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_traffic(w: workloads.Workload, fetch_csv: str, write_csv: str, copy_mib: int) -> int:
+    """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    each scaled by the ratio of the bytes a plain copy of copy_mib MiB moves
+    to what the same counter reads for that copy.  Per kernel, the median
+    over the dispatches of its most frequent instantiation (which outvotes
+    the single quantizer launch that prepares the weights)."""
+    if not copy_mib:
+        print("--traffic needs the --copy-mib the counter runs used", file=sys.stderr)
+        return 2
+    known = copy_mib << 20
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _counter_means(path, counter)
+        copies = [v for (kind, _), vs in vals.items() if kind == "copy" for v in vs]
+        if not copies:
+            print(f"no copy kernel in {path}", file=sys.stderr)
+            return 1
+        copy_kib = float(np.median(copies[-3:]))
+        scale = known / (copy_kib * 1024.0)
+        for kind in ("gemm", "quantize"):
+            inst = [(len(vs), name, vs) for (k, name), vs in vals.items() if k == kind]
+            if not inst:
+                continue
+            _, name, vs = max(inst)
+            rec = out.setdefault(kind, {"workload": w.name, "kernel": name,
+                                        "source_sha256_16": source_hash(KERNEL_SOURCES[kind])})
+            key = "fetch" if counter == "FETCH_SIZE" else "write"
+            rec[f"{key}_kib_per_dispatch"] = round(float(np.median(vs)), 1)
+            rec[f"{key}_copy_kib"] = round(copy_kib, 1)
+            rec[f"{key}_scale"] = round(scale, 4)
+            rec[f"{key}_bytes"] = int(float(np.median(vs)) * 1024.0 * scale)
+    for kind, rec in out.items():
+        rec["hbm_bytes_per_launch"] = rec.get("fetch_bytes", 0) + rec.get("write_bytes", 0)
+        path = os.path.join(PROFILE_DIR, f"traffic_{kind}_{w.name}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(path, json.dumps(rec))
+    return 0
+
+
 def to_dev_x(X: np.ndarray, torch):
     if X.dtype == np.uint16:
         return torch.from_numpy(X.view(np.int16)).to("cuda:0").view(torch.bfloat16)
@@ -107,9 +166,21 @@ def main() -> int:
     ap.add_argument("--workload", default="mlp_up", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated over steps (0: enough to exceed the Infinity Cache)")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="rows in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of X in the CPU oracle sample (0: all of them, one whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, pass a float32 tensor of this many MiB three times "
+                         "through torch.neg (a plain copy kernel of known size that calibrates "
+                         "the HBM byte counters)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter_collection CSVs of a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 run of this benchmark (with --copy-mib) into "
+                         "profiles/traffic_<kernel>_<workload>.json")
     args = ap.parse_args()
+    if args.traffic:
+        return write_traffic(workloads.WORKLOADS[args.workload], args.traffic[0],
+                             args.traffic[1], args.copy_mib)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the INT8 convrot linear is benchmarked on a "
@@ -152,45 +223,58 @@ def main() -> int:
         Ys = [torch.empty((w.M, w.N), dtype=torch.bfloat16 if yd == cr.BF16 else torch.float32,
                           device=dev) for _ in range(w.n_linears)]
         sets.append((Xd, ws, Ys))
-    m_pad = (w.M + 3) // 4 * 4
 
-    def step(i, ev=None):
+    def quantize(i):
         Xd, ws, Ys = sets[i % n_sets]
+        cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
+
+    def gemm(i):
+        Xd, ws, Ys = sets[i % n_sets]
+        l = lins[0]
+        qx, sx = views[i % n_sets]
+        cr.int8_linear(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
+
+    def step(i):
         if shared:
-            if ev is not None:
-                ev[0].record()
+            Xd, ws, Ys = sets[i % n_sets]
             cr.convrot_int8_linear_shared(
                 Xd, w.G, [dict(l, Y=Y) for l, Y in zip(lins, Ys)], workspace=ws)
-            if ev is not None:
-                ev[2].record()
-            return
-        l = lins[0]
-        if ev is not None:
-            ev[0].record()
-        cr.convrot_quantize_rows(Xd, w.G, l["input_scale"], packed=ws)
-        if ev is not None:
-            ev[1].record()
-        cr.int8_linear(ws[: m_pad * w.K].view(torch.int8).view(m_pad, w.K),
-                       ws[m_pad * w.K:m_pad * w.K + 4 * m_pad].view(torch.float32),
-                       l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
-        if ev is not None:
-            ev[2].record()
+        else:
+            quantize(i)
+            gemm(i)
 
+    views = [cr.packed_parts(ws, w.M, w.K) for _, ws, _ in sets]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K whole steps, HIP events only at its two ends (an event
+    # recorded between kernels leaves the GPU idle for a few microseconds)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        step(i, events[i])
+        step(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    ev_step_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    def kernel_us(fn):
+        """Average duration of one kernel: K launches of it back to back (same
+        input rotation as the steps) between two HIP events on its stream."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / args.steps
 
     ops = gemm_ops(w, w.n_linears)
-    qbytes = quantize_bytes(w) * n_packed
     rec = {
         "metric": "int8 linear TOPS + quantize GB/s (fraction of MI355X roofline), M=4096 K=3072",
         "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -209,10 +293,11 @@ def main() -> int:
                                f"{list(w.input_scales)}",
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,
                    "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets},
+        "step_us_events": round(ev_step_us, 3),
     }
     if not shared:
-        tq = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps * 1e-3
-        tg = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
+        tq = kernel_us(quantize) * 1e-6
+        tg = kernel_us(gemm) * 1e-6
         q_gbs = quantize_bytes(w) / tq / 1e9
         g_tops = ops / tg / 1e12
         rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -226,13 +311,17 @@ def main() -> int:
                            "us": round(tg * 1e6, 3),
                            "note": "int8 ops: one multiply-add counts as 2"}
     else:
-        tt = sum(e[0].elapsed_time(e[2]) for e in events) / args.steps * 1e-3
-        rec["step_us_events"] = round(tt * 1e6, 3)
         rec["roofline"] = None
         rec["quantize"] = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows or w.M)
     print(json.dumps(rec), flush=True)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)          # one read and one write of each element
+        torch.cuda.synchronize()
     return 0
 
 

@@ -78,9 +78,13 @@ def _torch():
     return torch
 
 
-def _stream(stream):
+def _stream(stream, t):
+    """The HIP stream to launch on: the given one, else torch's current
+    stream on the device of tensor t."""
+    if t.device.type != "cuda":
+        raise ValueError(f"expected tensors in GPU memory, got one on {t.device}")
     if stream is None:
-        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+        return ctypes.c_void_p(_torch()._C._cuda_getCurrentRawStream(t.device.index))
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
@@ -149,7 +153,7 @@ def convrot_quantize_rows(X, group_size: int, input_scale: float = 1.0, packed=N
     if packed is None:
         packed = torch.empty(convrot_packed_bytes(M, K), dtype=torch.uint8, device=X.device)
     rc = library().convrot_quantize_rows(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
-                                         ctypes.c_float(input_scale), _ptr(packed), _stream(stream))
+                                         ctypes.c_float(input_scale), _ptr(packed), _stream(stream, X))
     _check("convrot_quantize_rows", rc)
     return packed
 
@@ -166,7 +170,7 @@ def int8_linear(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, Y=No
     ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
     rc = library().int8_linear(_ptr(Qx), _ptr(s_x), M, K, _ptr(Qw), _ptr(s_w), _ptr(bias), N,
                                ctypes.c_float(input_scale), _ptr(Y), _dtype_code(Y), ldy,
-                               _stream(stream))
+                               _stream(stream, Y))
     _check("int8_linear", rc)
     return Y
 
@@ -178,7 +182,7 @@ def convrot_int8_gemm_i32(Qx, Qw, A=None, M: int | None = None, stream=None):
     N = Qw.shape[0]
     if A is None:
         A = torch.empty((M, N), dtype=torch.int32, device=Qw.device)
-    rc = library().convrot_int8_gemm_i32(_ptr(Qx), _ptr(Qw), M, K, N, _ptr(A), _stream(stream))
+    rc = library().convrot_int8_gemm_i32(_ptr(Qx), _ptr(Qw), M, K, N, _ptr(A), _stream(stream, A))
     _check("convrot_int8_gemm_i32", rc)
     return A
 
@@ -198,7 +202,7 @@ def convrot_int8_linear(X, group_size: int, input_scale: float, Qw, s_w=None, bi
     rc = library().convrot_int8_linear(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
                                        ctypes.c_float(input_scale), _ptr(Qw), _ptr(s_w), _ptr(bias),
                                        N, _ptr(Y), _dtype_code(Y), ldy, _ptr(workspace),
-                                       workspace.numel(), _stream(stream))
+                                       workspace.numel(), _stream(stream, X))
     _check("convrot_int8_linear", rc)
     return Y
 
@@ -236,6 +240,6 @@ def convrot_int8_linear_shared(X, group_size: int, linears, workspace=None, stre
                                 dtype=torch.uint8, device=X.device)
     rc = library().convrot_int8_linear_shared(_ptr(X), _dtype_code(X), M, K, ldx, group_size, n,
                                               descs, _ptr(workspace), workspace.numel(),
-                                              _stream(stream))
+                                              _stream(stream, X))
     _check("convrot_int8_linear_shared", rc)
     return outs

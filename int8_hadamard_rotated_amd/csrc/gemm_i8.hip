@@ -10,20 +10,20 @@
 // bias; weight scale and bias may be absent).  The unscale by the input scale
 // before the bias follows the convrot page's last paragraph of that section.
 //
-// Both operands are K-contiguous.  A workgroup of 4 waves computes a BM x BN
-// tile; waves form a 2 x 2 grid, each owning (BM/2) x (BN/2) as 16 x 16 MFMA
-// blocks (v_mfma_i32_16x16x64_i8, 64 K-bytes per instruction).  K advances in
-// 64-byte steps through two LDS buffers, with global loads staged in registers
-// two steps ahead.  The four 16-byte K chunks of each LDS row are XOR-swizzled
-// by row so that the fragment reads of consecutive rows hit distinct banks.
+// Structure.  Both operands are K-contiguous.  A workgroup of WM x WN waves
+// computes a BM x BN tile; wave (wm, wn) owns (BM/WM) x (BN/WN) as 16 x 16
+// blocks of v_mfma_i32_16x16x64_i8 (64 K-bytes per instruction).  K advances
+// in 64-byte steps through a 4-stage LDS ring filled by direct buffer-to-LDS
+// loads issued three steps ahead; fragments are read from LDS one step ahead
+// into registers.  The integer sum is exact whatever the order of K, so the
+// lane-to-K mapping inside an MFMA only has to agree between the two
+// operands, which are read with the same pattern.
 //
-// The integer sum is exact whatever the order of K, so the lane-to-K mapping
-// inside an MFMA only has to agree between the two operands, which are read
-// with the same pattern.  Several linears sharing one Q_x run in one launch:
-// the tile index space is the concatenation of every linear's tile grid.
-// Workgroups are renumbered so that each XCD (round-robin dispatch over 8)
-// receives a contiguous range of tiles, walked in groups of 4 tile rows, so
-// that tiles running together on one XCD share operand panels in its L2.
+// Several linears sharing one Q_x run in one launch: the tile index space is
+// the concatenation of every linear's tile grid.  Workgroups are renumbered
+// so that each XCD (round-robin dispatch over 8) receives a contiguous range
+// of tiles, walked in groups of 4 tile rows, so that tiles running together
+// on one XCD share operand panels in its L2.
 #pragma clang fp contract(off)
 
 #include "kernels.h"
@@ -33,46 +33,48 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kBK = 64;                    // K bytes per step (one MFMA K)
 
-template <int BM, int BN, int BK>
+template <int BM, int BN, int WM, int WN>
 struct Tile {
-    static constexpr int kWaveM = BM / 2;
-    static constexpr int kWaveN = BN / 2;
-    static constexpr int kTM = kWaveM / 16;
-    static constexpr int kTN = kWaveN / 16;
-    static constexpr int kStride = BK;                    // LDS bytes per row (swizzled)
-    static constexpr int kChunksPerRow = BK / 16;
-    static constexpr int kAChunks = BM * kChunksPerRow / kThreads;
-    static constexpr int kBChunks = BN * kChunksPerRow / kThreads;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kWaveM = BM / WM;
+    static constexpr int kWaveN = BN / WN;
+    static constexpr int kTM = kWaveM / 16;                // A blocks per wave
+    static constexpr int kTN = kWaveN / 16;                // B blocks per wave
+    static constexpr int kStride = kBK;                    // LDS bytes per row (swizzled)
     static constexpr int kStageBytes = (BM + BN) * kStride;
     static constexpr int kStages = 4;                      // LDS ring depth
-    static constexpr int kLoads = (BM + BN) / 64;          // DMA loads per wave per step
-    static constexpr int kScaleOff = kStages * kStageBytes;  // s_x [BM], s_w [BN], bias [BN]
+    static constexpr int kLoads = (BM + BN) / (16 * kWaves);   // DMA loads per wave per step
+    static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w [BN], bias [BN]
     static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 2 * BN);
-    static_assert(BM * kChunksPerRow % kThreads == 0 && BN * kChunksPerRow % kThreads == 0, "");
-    static_assert(BK == 64, "one 16x16x64 MFMA K-step per LDS stage; the swizzle assumes 4 chunks");
+    static_assert((BM + BN) % (16 * kWaves) == 0, "whole 16-row DMA blocks per wave");
+    static_assert(BM % 16 == 0 && kWaveM % 16 == 0 && kWaveN % 16 == 0, "");
+    static_assert(kLoads <= kTM, "at most one DMA load per MFMA group");
+    static_assert((BM + 2 * BN) % 64 == 0, "64-float scale segments");
+    static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 };
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
 // Raw buffer descriptor (stride 0, 32-bit data format) over [base, base + bytes).
-__device__ __forceinline__ v4u buffer_rsrc(const int8_t *base, uint32_t bytes)
+__device__ __forceinline__ v4u buffer_rsrc(const void *base, uint32_t bytes)
 {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferFlags};
 }
 
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.
-// Issued as inline assembly so that the compiler does not serialize its LDS
-// reads behind these loads; the matching waits are explicit (wait_vmcnt).
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  Issued as inline assembly so that the
+// compiler does not hold its LDS reads behind these loads; the matching waits
+// are explicit (wait_vmcnt).  Offsets outside the descriptor read as zero.
 __device__ __forceinline__ void dma_x4(v4u rsrc, int voff, int soff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
@@ -104,12 +106,11 @@ __device__ __forceinline__ void wait_vmcnt()
 // low-bit-XOR layouts, which cost two LDS passes per read.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
-
-template <int BM, int BN, int BK, bool DIV>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int tiles_m,
-                                                              int total_tiles)
+template <int BM, int BN, int WM, int WN, bool DIV>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
+    GemmProblem p, int tiles_m, int total_tiles)
 {
-    using T = Tile<BM, BN, BK>;
+    using T = Tile<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(16))) int8_t lds[T::kLdsBytes];
 
     // ---- tile assignment: contiguous tile range per XCD, then group-M order
@@ -131,27 +132,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
 
     const int64_t M = p.M, K = p.K, N = L.N;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
 
-    // ---- global -> LDS by direct buffer loads (buffer_load_dwordx4 ... lds):
-    // lane L of a wave writes LDS bytes [M0 + 16 L, M0 + 16 L + 16).  One
-    // instruction of wave w fills the 1 KB of rows 64 i + 16 w .. +16 of an
-    // operand tile; the lane's slot (row L/4, slot L%4) receives logical chunk
-    // (L%4) ^ swz(row), so the rows' 16-byte K chunks are XOR-swizzled and the
-    // fragment reads of consecutive rows hit distinct bank groups.  swz(row)
-    // only depends on row bits 1..2, that is on L/4.
+    // ---- global -> LDS by direct buffer loads.  A stage holds the BM rows
+    // of the A tile followed by the BN rows of the B tile, 64 bytes each; the
+    // DMA instruction g of a step moves rows 16 g .. 16 g + 15 of that list
+    // (1 KB): lane L writes row 16 g + L/4, slot L%4, which receives logical
+    // K chunk (L%4) ^ swz(row).  swz only depends on row bits 1..2, that is on
+    // L/4, so one per-lane offset serves every instruction.  Wave w issues
+    // instructions g = kWaves * q + w, q < kLoads.
     //
     // Each operand tile is addressed through a buffer descriptor that starts
     // at the tile's first row and ends after its last valid row; rows past M
     // (or N) fall outside it and are never stored.
-    //
-    // kStages LDS stages form a ring: step ks lives in stage ks % kStages and
-    // its loads are issued kStages - 1 steps ahead.  Before step ks a wave
-    // waits until its own loads for ks have landed (vmcnt), then the barrier
-    // makes every wave's loads visible and also guarantees that every wave is
-    // done with step ks - 1, whose stage the loads for ks + kStages - 1 reuse.
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int64_t a_rows = (M - m0) < BM ? (M - m0) : BM;
     const int64_t b_rows = (N - n0) < BN ? (N - n0) : BN;
     const v4u a_rsrc = buffer_rsrc(p.Qx + m0 * K, (uint32_t)(a_rows * K));
@@ -160,24 +155,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
     const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t *)lds;
 
-    // load q (< kLoads) of a K-step: A rows for q < BM/64, else B rows
     auto issue_one = [&](int64_t step, int q) {
         const uint32_t st = lds_base + (uint32_t)(step % T::kStages) * T::kStageBytes;
-        const int k0 = (int)(step * BK);
-        if (q < BM / 64) {
-            dma_x4(a_rsrc, ld_voff, (64 * q + 16 * wave_u) * (int)K + k0,
-                   st + (64 * q + 16 * wave_u) * T::kStride);
-        } else {
-            const int qb = q - BM / 64;
-            dma_x4(b_rsrc, ld_voff, (64 * qb + 16 * wave_u) * (int)K + k0,
-                   st + BM * T::kStride + (64 * qb + 16 * wave_u) * T::kStride);
-        }
+        const int k0 = (int)(step * kBK);
+        const int g = T::kWaves * q + wave;
+        if (16 * g < BM)
+            dma_x4(a_rsrc, ld_voff, 16 * g * (int)K + k0, st + 16 * g * T::kStride);
+        else
+            dma_x4(b_rsrc, ld_voff, (16 * g - BM) * (int)K + k0, st + 16 * g * T::kStride);
     };
-    auto issue = [&](int64_t step) {
+
+    // The epilogue's row scales, weight scales and bias go to LDS first, by
+    // the same DMA path (64 floats per instruction), so that their latency is
+    // hidden behind the whole main loop.  They are older than every operand
+    // load, so the first operand wait also covers them.
+    const bool want_sx = L.out_kind != kOutI32;
+    const bool has_sw = L.s_w != nullptr, has_bias = L.bias != nullptr;
+    {
+        constexpr int kSeg = (BM + 2 * BN) / 64;
+        const v4u sx_rsrc = buffer_rsrc(want_sx ? p.s_x + m0 : nullptr,
+                                        want_sx ? (uint32_t)(a_rows * 4) : 0u);
+        const v4u sw_rsrc = buffer_rsrc(has_sw ? L.s_w + n0 : nullptr,
+                                        has_sw ? (uint32_t)(b_rows * 4) : 0u);
+        const v4u bi_rsrc = buffer_rsrc(has_bias ? L.bias + n0 : nullptr,
+                                        has_bias ? (uint32_t)(b_rows * 4) : 0u);
 #pragma unroll
-        for (int q = 0; q < T::kLoads; ++q)
-            issue_one(step, q);
-    };
+        for (int q = 0; q < kSeg; ++q) {
+            if (q % T::kWaves != wave)
+                continue;
+            const uint32_t dst = lds_base + T::kScaleOff + 256 * q;
+            if (q < BM / 64) {
+                if (want_sx)
+                    dma_x1(sx_rsrc, 4 * lane, 256 * q, dst);
+            } else if (q < (BM + BN) / 64) {
+                if (has_sw)
+                    dma_x1(sw_rsrc, 4 * lane, 256 * (q - BM / 64), dst);
+            } else if (has_bias) {
+                dma_x1(bi_rsrc, 4 * lane, 256 * (q - (BM + BN) / 64), dst);
+            }
+        }
+    }
 
     v4i acc[T::kTM][T::kTN];
 #pragma unroll
@@ -191,86 +208,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
     const int frag_row = lane & 15, frag_chunk = lane >> 4;
     const int frag_slot = 16 * (frag_chunk ^ swz(frag_row));
     const int a_frag0 = (wm * T::kWaveM + frag_row) * T::kStride + frag_slot;
-    const int b_frag0 = BM * T::kStride + (wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
+    const int b_frag0 = (BM + wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
+    auto read_a = [&](int stage, int i) {
+        return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + a_frag0 +
+                                              i * 16 * T::kStride);
+    };
+    auto read_b = [&](int stage, int j) {
+        return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + b_frag0 +
+                                              j * 16 * T::kStride);
+    };
 
-    // ---- main loop.  One K-step: every fragment read is issued first (A
-    // block 0 and the B blocks lead, so the first MFMA waits for two reads
-    // only), then the MFMAs run as kTM groups, one per A block.  When `next`
-    // is a valid step its kLoads DMA loads are spread over the first groups
-    // so that the vector-memory queue drains while the matrix cores work.
-    static_assert(T::kLoads <= T::kTM, "at most one load per MFMA group");
-    auto step_body = [&](int stage, int64_t next) {
-        const int8_t *base = lds + stage * T::kStageBytes;
-        v4i fa[T::kTM], fb[T::kTN];
-        fa[0] = *reinterpret_cast<const v4i *>(base + a_frag0);
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j)
-            fb[j] = *reinterpret_cast<const v4i *>(base + b_frag0 + j * 16 * T::kStride);
-#pragma unroll
-        for (int i = 1; i < T::kTM; ++i)
-            fa[i] = *reinterpret_cast<const v4i *>(base + a_frag0 + i * 16 * T::kStride);
+    // ---- main loop, software-pipelined one K-step ahead on fragments.
+    // Iteration k multiplies step k from registers (A block i in fa[i], B
+    // block j in fb[j]) in row-major (i, j) order.  At its top the wave waits
+    // for its own DMA loads of step k+1 and passes the barrier that
+    // certifies everyone's; it then reads step k+1's fragments into the same
+    // registers as soon as their last use in step k has been issued: fa[i]
+    // after A block i's group and fb[j] right after MFMA (kTM-1, j).  That
+    // barrier also shows that every wave has consumed step k-1's fragments
+    // (it has issued all of iteration k-1's MFMAs), so the DMA loads of step
+    // k+3, spread one per MFMA group, may overwrite stage (k-1) % 4: loads
+    // are issued two iterations before the barrier that needs them.
+    static_assert(T::kStages == 4, "ring depth assumed by the wait counts");
+    v4i fa[T::kTM], fb[T::kTN];
+    const int64_t ksteps = K / kBK;
+    auto iteration = [&](int64_t k) {
+        const bool has_next = k + 1 < ksteps;
+        if (has_next) {
+            if (k + 2 < ksteps)
+                wait_vmcnt<T::kLoads>();       // step k+2's loads may stay in flight
+            else
+                wait_vmcnt<0>();
+            __syncthreads();
+        }
+        const int next_stage = (int)((k + 1) % T::kStages);
+        const int64_t dma_step = k + 3;
+        const bool dma = dma_step < ksteps;
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            if (next >= 0 && i < T::kLoads)
-                issue_one(next, i);
+            if (dma && i < T::kLoads)
+                issue_one(dma_step, i);
 #pragma unroll
-            for (int j = 0; j < T::kTN; ++j)
+            for (int j = 0; j < T::kTN; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                if (i == T::kTM - 1 && has_next)
+                    fb[j] = read_b(next_stage, j);
+            }
+            if (has_next)
+                fa[i] = read_a(next_stage, i);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // The epilogue's row scales, weight scales and bias go to LDS first, by
-    // the same DMA path (64 floats per instruction), so that their latency is
-    // hidden behind the whole main loop.  They are older than every operand
-    // load, so the first operand wait also covers them.
-    const bool want_sx = L.out_kind != kOutI32;
-    const bool has_sw = L.s_w != nullptr, has_bias = L.bias != nullptr;
-    {
-        constexpr int kSeg = (BM + 2 * BN) / 64;        // 64-float segments
-        const v4u sx_rsrc = buffer_rsrc(reinterpret_cast<const int8_t *>(p.s_x + (want_sx ? m0 : 0)),
-                                        want_sx ? (uint32_t)(a_rows * 4) : 0u);
-        const v4u sw_rsrc = buffer_rsrc(reinterpret_cast<const int8_t *>(L.s_w + (has_sw ? n0 : 0)),
-                                        has_sw ? (uint32_t)(b_rows * 4) : 0u);
-        const v4u b_rsrc2 = buffer_rsrc(reinterpret_cast<const int8_t *>(L.bias + (has_bias ? n0 : 0)),
-                                        has_bias ? (uint32_t)(b_rows * 4) : 0u);
-#pragma unroll
-        for (int q = 0; q < kSeg; ++q) {
-            if (q % 4 != wave_u)
-                continue;
-            const uint32_t dst = lds_base + T::kScaleOff + 256 * q;
-            if (q < BM / 64) {
-                if (want_sx)
-                    dma_x1(sx_rsrc, 4 * lane, 256 * q, dst);
-            } else if (q < (BM + BN) / 64) {
-                if (has_sw)
-                    dma_x1(sw_rsrc, 4 * lane, 256 * (q - BM / 64), dst);
-            } else if (has_bias) {
-                dma_x1(b_rsrc2, 4 * lane, 256 * (q - (BM + BN) / 64), dst);
-            }
-        }
-    }
-
-    const int64_t ksteps = K / BK;
 #pragma unroll
     for (int s0 = 0; s0 < T::kStages - 1; ++s0)
         if (s0 < ksteps)
-            issue(s0);
-    for (int64_t ks = 0; ks < ksteps; ++ks) {
-        // loads issued after step ks's: those of steps ks+1 .. min(ks+kStages-2, last)
-        const int64_t last = ksteps - 1 < ks + T::kStages - 2 ? ksteps - 1 : ks + T::kStages - 2;
-        const int64_t later = last - ks;
-        if (later >= 2)
-            wait_vmcnt<2 * T::kLoads>();
-        else if (later == 1)
-            wait_vmcnt<T::kLoads>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();
-        const int64_t next = ks + T::kStages - 1;
-        step_body((int)(ks % T::kStages), next < ksteps ? next : -1);
-    }
+#pragma unroll
+            for (int q = 0; q < T::kLoads; ++q)
+                issue_one(s0, q);
+    if (ksteps > 2)
+        wait_vmcnt<2 * T::kLoads>();
+    else if (ksteps > 1)
+        wait_vmcnt<T::kLoads>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < T::kTM; ++i)
+        fa[i] = read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < T::kTN; ++j)
+        fb[j] = read_b(0, j);
+    for (int64_t k = 0; k < ksteps; ++k)
+        iteration(k);
     __syncthreads();
 
     // ---- epilogue.  The MFMA 16x16 result block leaves lane l with column
@@ -278,17 +289,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
     // accumulators in its own LDS region (the operand ring is free by now),
     // then reads it back four consecutive columns per lane: slot s of a slice
     // is (row s / kColQuads, column quad s % kColQuads), and lane l owns slots
-    // l + 64 k.  Half a wave then covers a full 128-column row, so every store
-    // instruction writes whole row segments (256 contiguous bytes for bf16),
-    // the pattern the memory system absorbs at full rate.  The staging region
-    // is private to the wave and LDS operations of one wave complete in
-    // order, so no barrier is needed between writing and reading it.
+    // l + 64 k.  Lanes covering one row then store whole row segments (256
+    // contiguous bytes of bf16 for a 128-column wave tile), the pattern the
+    // memory system absorbs at full rate; 32-byte row pieces per instruction
+    // measured at well under half of it.  The staging region is private to
+    // the wave and LDS operations of one wave complete in order, so no
+    // barrier separates writing and reading it.
     constexpr int kStageStride = T::kWaveN + 4;                 // int32 per staged row
     constexpr int kColQuads = T::kWaveN / 4;
     constexpr int kSlots = 16 * kColQuads / 64;
     constexpr int kRowStep = 64 / kColQuads;
-    static_assert(64 % kColQuads == 0, "");
-    static_assert(4 * 16 * kStageStride * 4 <= T::kScaleOff, "staging fits in the ring");
+    static_assert(64 % kColQuads == 0 && kSlots >= 1, "");
+    static_assert(T::kWaves * 16 * kStageStride * 4 <= T::kScaleOff, "staging fits in the ring");
     int32_t *stage = reinterpret_cast<int32_t *>(lds) + wave * 16 * kStageStride;
     const float *sx_lds = reinterpret_cast<const float *>(lds + T::kScaleOff);
     const float *sw_lds = sx_lds + BM;
@@ -354,10 +366,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
                         y[e] = t[e];
                 }
             } else {
-                // round to nearest even (the hardware conversion; finite inputs)
-                // Both halves are taken from the packed words with integer
-                // operations (element extraction from a bf16 vector is
-                // miscompiled for the high half by this toolchain).
+                // Round to nearest even (the hardware conversion, finite
+                // inputs).  Both halves are taken from the packed words with
+                // integer operations: extracting the high element of a bf16
+                // vector is miscompiled by this toolchain.
                 const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
                 const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
                 uint16_t *y = static_cast<uint16_t *>(Yv) + r * ldy + o;
@@ -373,9 +385,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(GemmProblem p, int
     }
 }
 
-template <int BM, int BN, int BK>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
 {
+    using T = Tile<BM, BN, WM, WN>;
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     int total = 0;
     for (int d = 0; d < p.n_lin; ++d) {
@@ -390,11 +403,11 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     for (int d = 0; d < p.n_lin; ++d)
         div = div || p.lin[d].alpha != 1.0f;
     if (div)
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, true>), dim3(total), dim3(kThreads), 0,
-                           stream, p, tiles_m, total);
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, true>), dim3(total), dim3(T::kThreads),
+                           0, stream, p, tiles_m, total);
     else
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, false>), dim3(total), dim3(kThreads), 0,
-                           stream, p, tiles_m, total);
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, false>), dim3(total), dim3(T::kThreads),
+                           0, stream, p, tiles_m, total);
     return hipGetLastError();
 }
 
@@ -402,14 +415,16 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
 
 hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
 {
-    // Large grids use 256 x 256 tiles; grids too small to cover the 256 CUs
-    // with them fall back to 128 x 128.
+    // Large grids use 256 x 256 tiles computed by 16 waves (4 x 4, four per
+    // SIMD, so that one wave's LDS and barrier waits are covered by the MFMAs
+    // of the others); grids too small to cover the 256 CUs with them fall
+    // back to 128 x 128 tiles with 4 waves.
     int64_t big = 0;
     for (int d = 0; d < p.n_lin; ++d)
         big += ((p.M + 255) / 256) * ((p.lin[d].N + 255) / 256);
     if (big >= 256)
-        return launch_tiled<256, 256, 64>(p, stream);
-    return launch_tiled<128, 128, 64>(p, stream);
+        return launch_tiled<256, 256, 4, 4>(p, stream);
+    return launch_tiled<128, 128, 2, 2>(p, stream);
 }
 
 }  // namespace convrot_detail
