@@ -233,6 +233,207 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
     }
 }
 
+// ---- binary32 inputs: the same arithmetic with the row data staged in LDS.
+//
+// A wave's 16 quads own 16 consecutive spans (16 KB of binary32).  The quad
+// layout above makes every load instruction touch two 32-byte pieces per
+// quad; here each load instruction instead reads 64 consecutive 16-byte
+// pieces (1 KB), which the memory system serves at a clearly higher rate.
+// The pieces go to a wave-private LDS region and each lane reads back its own
+// chunks; the codes take the same route in reverse, so stores are also 1 KB
+// per instruction.  LDS operations of one wave complete in order, so the
+// region needs no barrier.  Odd quads store their pieces with the slot index
+// XOR-ed by one (codes: by 4 * (quad % 4)) so that the lanes of one read
+// instruction spread over distinct LDS banks.
+template <int G, int NC, bool SCALED>
+__global__ __launch_bounds__(256) void quantize_rows_staged(
+    const float *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
+    int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
+{
+    static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
+    static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    constexpr int kPC = 2;                                // 16-B pieces per 8-element chunk
+    constexpr int kQuadPieces = 4 * NC * kPC;            // 16-B input pieces per quad span
+    constexpr int kWavePieces = 16 * kQuadPieces;        // per wave
+    constexpr int kLoadsPerLane = kWavePieces / 64;      // = NC * kPC
+    constexpr int kOutPieces = 16 * (32 * NC / 16);      // 16-B code pieces per wave
+    constexpr int kStoresPerLane = kOutPieces / 64;      // = NC / 2
+    extern __shared__ __attribute__((aligned(16))) unsigned char stage_lds[];
+    __shared__ unsigned row_max[256];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int quad = tid >> 2;
+    const int j0 = tid & 1, j1 = (tid >> 1) & 1;
+    const int n_quads = quads_per_row * rows_per_wg;
+    const int row_local = quad / quads_per_row;
+    const int q_in_row = quad - row_local * quads_per_row;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row = row0 + row_local;
+    const bool live = row < M;
+    unsigned char *wst = stage_lds + wave * (kWavePieces * 16);
+    constexpr int kFlip = 1;
+
+    if (tid < rows_per_wg)
+        row_max[tid] = 0u;
+
+    // contiguous loads: lane L, instruction i takes wave piece p = 64 i + L
+    using Raw = v4u;
+    Raw raw[kLoadsPerLane];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int p = 64 * i + lane;
+        const int qw = 16 * wave + p / kQuadPieces;            // quad within the workgroup
+        const int rl = qw / quads_per_row;
+        const int64_t r = row0 + rl;
+        if (qw < n_quads && r < M) {
+            const int qi = qw - rl * quads_per_row;
+            const unsigned char *src = reinterpret_cast<const unsigned char *>(X + r * ldx + (int64_t)qi * (32 * NC)) +
+                                       16 * (p % kQuadPieces);
+            raw[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw *>(src));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int p = 64 * i + lane;
+        const int ql = p / kQuadPieces, pi = p % kQuadPieces;
+        *reinterpret_cast<Raw *>(wst + 16 * (ql * kQuadPieces + (pi ^ (kFlip * (ql & 1))))) = raw[i];
+    }
+    __syncthreads();   // row_max cleared (the staging region is wave-private)
+
+    const int ql_me = (tid >> 2) & 15;                          // my quad within the wave
+    float v[NC][8];
+    if (live) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);   // element offset in the span
+#pragma unroll
+            for (int h = 0; h < kPC; ++h) {
+                const int pi = e / 4 + h;
+                const Raw u = *reinterpret_cast<const Raw *>(wst + 16 * (ql_me * kQuadPieces + (pi ^ (kFlip * (ql_me & 1)))));
+                // the element is converted to a value before the bit cast:
+                // a bit cast of a vector element lvalue reads element 0 with
+                // this toolchain
+                const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    v[c][4 * h + t] = __builtin_bit_cast(float, w[t]);
+            }
+        }
+
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    v[c][p] = v[c][p] * alpha;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
+            h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
+        }
+        if constexpr (G >= 16) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    h4_split<kQuadPermXor1>(v[c][p], v[c][p + 4]);
+        }
+        if constexpr (G >= 64) {
+#pragma unroll
+            for (int c = 0; c < NC; c += 2)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    h4_split<kQuadPermXor2>(v[c][p], v[c + 1][p]);
+        }
+        if constexpr (G >= 256) {
+#pragma unroll
+            for (int c0 = 0; c0 < 2; ++c0)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    h4_local(v[c0][p], v[c0 + 2][p], v[c0 + 4][p], v[c0 + 6][p]);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                m = fmaxf(m, fabsf(v[c][p]));
+        m = fmaxf(m, quad_swap<kQuadPermXor1>(m));
+        m = fmaxf(m, quad_swap<kQuadPermXor2>(m));
+        if ((tid & 3) == 0)
+            atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
+    }
+    __syncthreads();
+
+    // codes: 8 bytes per chunk into the wave's staging region (32 NC bytes per
+    // quad), then contiguous 16-B stores
+    constexpr int kQuadOut = 32 * NC / 16;                      // 16-B code pieces per quad
+    if (row < M_pad) {
+        unsigned char *qst = wst + 16 * ql_me * kQuadOut;
+        if (!live) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int o = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
+                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = v2u{0u, 0u};
+            }
+            if (q_in_row == 0 && (tid & 3) == 0)
+                S[row] = 0.0f;
+        } else {
+            const float m = __builtin_bit_cast(float, row_max[row_local]);
+            const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
+            if (q_in_row == 0 && (tid & 3) == 0)
+                S[row] = __fdiv_rn(m, 127.0f);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                unsigned w[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const float t = v[c][p] * inv;
+                    w[p] = __builtin_bit_cast(unsigned, t + 12582912.0f);
+                }
+                v2u out;
+                out.x = pack_low_bytes(w[0], w[1], w[2], w[3]);
+                out.y = pack_low_bytes(w[4], w[5], w[6], w[7]);
+                const int o = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
+                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = out;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kStoresPerLane; ++i) {
+        const int p = 64 * i + lane;                            // wave code piece
+        const int ql = p / kQuadOut, pi = p % kQuadOut;
+        const int qw = 16 * wave + ql;
+        const int rl = qw / quads_per_row;
+        const int64_t r = row0 + rl;
+        if (qw < n_quads && r < M_pad) {
+            const int qi = qw - rl * quads_per_row;
+            const v4u val = *reinterpret_cast<const v4u *>(wst + 16 * (ql * kQuadOut + (pi ^ (4 * (ql & 3) % kQuadOut))));
+            *reinterpret_cast<v4u *>(Q + r * K + (int64_t)qi * (32 * NC) + 16 * pi) = val;
+        }
+    }
+}
+
+// LDS bytes per wave of the staged kernel (16 quads of 32 NC binary32 values).
+template <int NC>
+constexpr size_t kStagedWaveBytes = 16 * 32 * NC * 4;
+
+template <int G, int NC>
+void launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alpha, int8_t *Q,
+                   float *S, int64_t m_pad, int qr, int rows, hipStream_t stream)
+{
+    const int threads = 4 * qr * rows;
+    const size_t lds = (size_t)((threads + 63) / 64) * kStagedWaveBytes<NC>;
+    const int64_t blocks = (m_pad + rows - 1) / rows;
+    if (alpha != 1.0f)
+        hipLaunchKernelGGL((quantize_rows_staged<G, NC, true>), dim3((unsigned)blocks), dim3(threads), lds,
+                           stream, X, M, m_pad, K, ldx, alpha, Q, S, qr, rows);
+    else
+        hipLaunchKernelGGL((quantize_rows_staged<G, NC, false>), dim3((unsigned)blocks), dim3(threads), lds,
+                           stream, X, M, m_pad, K, ldx, alpha, Q, S, qr, rows);
+}
+
 int gcd_int(int a, int b)
 {
     while (b) {
@@ -259,6 +460,12 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
     const int64_t blocks = (m_pad + rows - 1) / rows;
     int8_t *Q = static_cast<int8_t *>(packed);
     float *S = reinterpret_cast<float *>(Q + m_pad * K);
+    if constexpr (sizeof(XT) == 4) {
+        // binary32 rows of up to 256 threads per workgroup take the staged kernel
+        if (threads <= 256)
+            return launch_staged<G, NC>(static_cast<const float *>(X), M, K, ldx, alpha, Q, S, m_pad,
+                                        qr, rows, stream);
+    }
     if (alpha != 1.0f)
         hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,

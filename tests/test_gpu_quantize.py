@@ -34,8 +34,9 @@ def test_workload_packed_bit_exact(orc, name):
         assert_bits_equal(got, want, f"{name} packed (alpha={alpha})")
 
 
-EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (129, 3072), (7, 12288),
-               (2, 65536)]
+# K = 4096 and 8192 fill a 256-thread workgroup (4 waves) of the staged binary32 kernel
+EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (129, 3072), (9, 4096),
+               (6, 8192), (7, 12288), (2, 65536)]
 
 
 @pytest.mark.parametrize("G", [4, 16, 64, 256])
