@@ -43,7 +43,7 @@ constexpr int kGroupM = 4;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kBK = 64;                    // K bytes per step (one MFMA K)
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 struct Tile {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
@@ -53,13 +53,14 @@ struct Tile {
     static constexpr int kTN = kWaveN / 16;                // B blocks per wave
     static constexpr int kStride = kBK;                    // LDS bytes per row (swizzled)
     static constexpr int kStageBytes = (BM + BN) * kStride;
-    static constexpr int kStages = 4;                      // LDS ring depth
+    static constexpr int kStages = STAGES;                 // LDS ring depth
     static constexpr int kLoads = (BM + BN) / (16 * kWaves);   // DMA loads per wave per step
     static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w [BN], bias [BN]
     static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 2 * BN);
     static_assert((BM + BN) % (16 * kWaves) == 0, "whole 16-row DMA blocks per wave");
     static_assert(BM % 16 == 0 && kWaveM % 16 == 0 && kWaveN % 16 == 0, "");
     static_assert(kLoads <= kTM, "at most one DMA load per MFMA group");
+    static_assert(STAGES >= 4, "ring depth");
     static_assert((BM + 2 * BN) % 64 == 0, "64-float scale segments");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 };
@@ -106,11 +107,26 @@ __device__ __forceinline__ void wait_vmcnt()
 // low-bit-XOR layouts, which cost two LDS passes per read.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
-template <int BM, int BN, int WM, int WN, bool DIV>
+// Wait until at most n of this wave's DMA loads are outstanding (n a
+// multiple of LOADS, at most MAXN).
+template <int LOADS, int MAXN>
+__device__ __forceinline__ void wait_vmcnt_le(int n)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= MAXN)
+            wait_vmcnt<MAXN>();
+        else
+            wait_vmcnt_le<LOADS, MAXN - LOADS>(n);
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool DIV>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     GemmProblem p, int tiles_m, int total_tiles)
 {
-    using T = Tile<BM, BN, WM, WN>;
+    using T = Tile<BM, BN, WM, WN, STAGES>;
     __shared__ __attribute__((aligned(16))) int8_t lds[T::kLdsBytes];
 
     // ---- tile assignment: contiguous tile range per XCD, then group-M order
@@ -155,9 +171,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t *)lds;
 
-    auto issue_one = [&](int64_t step, int q) {
+    auto issue_one = [&](int step, int q) {
         const uint32_t st = lds_base + (uint32_t)(step % T::kStages) * T::kStageBytes;
-        const int k0 = (int)(step * kBK);
+        const int k0 = step * kBK;
         const int g = T::kWaves * q + wave;
         if (16 * g < BM)
             dma_x4(a_rsrc, ld_voff, 16 * g * (int)K + k0, st + 16 * g * T::kStride);
@@ -227,22 +243,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // after A block i's group and fb[j] right after MFMA (kTM-1, j).  That
     // barrier also shows that every wave has consumed step k-1's fragments
     // (it has issued all of iteration k-1's MFMAs), so the DMA loads of step
-    // k+3, spread one per MFMA group, may overwrite stage (k-1) % 4: loads
-    // are issued two iterations before the barrier that needs them.
-    static_assert(T::kStages == 4, "ring depth assumed by the wait counts");
+    // k + S - 1 (S = ring depth), spread one per MFMA group, may overwrite
+    // stage (k-1) % S: loads are issued S - 2 iterations before the barrier
+    // that needs them.
+    constexpr int S = T::kStages;
+    static_assert((S - 2) * T::kLoads < 64, "vmcnt range");
     v4i fa[T::kTM], fb[T::kTN];
-    const int64_t ksteps = K / kBK;
-    auto iteration = [&](int64_t k) {
+    const int ksteps = (int)(K / kBK);
+    auto iteration = [&](int k) {
         const bool has_next = k + 1 < ksteps;
         if (has_next) {
-            if (k + 2 < ksteps)
-                wait_vmcnt<T::kLoads>();       // step k+2's loads may stay in flight
-            else
-                wait_vmcnt<0>();
+            // step k+1 must have landed; steps k+2 .. k+S-2 may stay in flight
+            const int younger = (ksteps - k - 2) < (S - 3) ? (ksteps - k - 2) : (S - 3);
+            wait_vmcnt_le<T::kLoads, (S - 3) * T::kLoads>(younger * T::kLoads);
             __syncthreads();
         }
-        const int next_stage = (int)((k + 1) % T::kStages);
-        const int64_t dma_step = k + 3;
+        const int next_stage = (k + 1) % S;
+        const int dma_step = k + S - 1;
         const bool dma = dma_step < ksteps;
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
@@ -262,17 +279,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     };
 
 #pragma unroll
-    for (int s0 = 0; s0 < T::kStages - 1; ++s0)
+    for (int s0 = 0; s0 < S - 1; ++s0)
         if (s0 < ksteps)
 #pragma unroll
             for (int q = 0; q < T::kLoads; ++q)
                 issue_one(s0, q);
-    if (ksteps > 2)
-        wait_vmcnt<2 * T::kLoads>();
-    else if (ksteps > 1)
-        wait_vmcnt<T::kLoads>();
-    else
-        wait_vmcnt<0>();
+    {
+        // step 0 must have landed (and the older scale loads)
+        const int younger = (ksteps - 1) < (S - 2) ? (ksteps - 1) : (S - 2);
+        wait_vmcnt_le<T::kLoads, (S - 2) * T::kLoads>(younger * T::kLoads);
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
@@ -280,7 +296,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
     for (int j = 0; j < T::kTN; ++j)
         fb[j] = read_b(0, j);
-    for (int64_t k = 0; k < ksteps; ++k)
+    for (int k = 0; k < ksteps; ++k)
         iteration(k);
     __syncthreads();
 
@@ -385,10 +401,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
 {
-    using T = Tile<BM, BN, WM, WN>;
+    using T = Tile<BM, BN, WM, WN, STAGES>;
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     int total = 0;
     for (int d = 0; d < p.n_lin; ++d) {
@@ -403,10 +419,10 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     for (int d = 0; d < p.n_lin; ++d)
         div = div || p.lin[d].alpha != 1.0f;
     if (div)
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, true>), dim3(total), dim3(T::kThreads),
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, true>), dim3(total), dim3(T::kThreads),
                            0, stream, p, tiles_m, total);
     else
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, false>), dim3(total), dim3(T::kThreads),
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, false>), dim3(total), dim3(T::kThreads),
                            0, stream, p, tiles_m, total);
     return hipGetLastError();
 }
@@ -418,13 +434,16 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
     // Large grids use 256 x 256 tiles computed by 16 waves (4 x 4, four per
     // SIMD, so that one wave's LDS and barrier waits are covered by the MFMAs
     // of the others); grids too small to cover the 256 CUs with them fall
-    // back to 128 x 128 tiles with 4 waves.
+    // back to 128 x 128 tiles with 8 waves (2 x 4; 64 KB of LDS, so two
+    // workgroups fit on a CU).  Both use a 4-stage ring: measured on gfx950,
+    // deeper rings (6 or 8 stages) were slower for every shape tried once
+    // they cost the second resident workgroup, and no faster otherwise.
     int64_t big = 0;
     for (int d = 0; d < p.n_lin; ++d)
         big += ((p.M + 255) / 256) * ((p.lin[d].N + 255) / 256);
     if (big >= 256)
-        return launch_tiled<256, 256, 4, 4>(p, stream);
-    return launch_tiled<128, 128, 2, 2>(p, stream);
+        return launch_tiled<256, 256, 4, 4, 4>(p, stream);
+    return launch_tiled<128, 128, 2, 4, 4>(p, stream);
 }
 
 }  // namespace convrot_detail
