@@ -85,7 +85,7 @@ def _counter_means(path: str, counter: str) -> dict:
                 continue
             name = r["Kernel_Name"]
             kind = ("gemm" if "gemm_i8_kernel" in name else
-                    "quantize" if "quantize_rows_kernel" in name else
+                    "quantize" if "quantize_rows" in name else
                     "copy" if "elementwise" in name and "neg" in name else None)
             if kind is not None:
                 vals.setdefault((kind, name), []).append(float(r["Counter_Value"]))
