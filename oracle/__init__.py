@@ -85,7 +85,8 @@ class Oracle:
     """ctypes wrapper over a built oracle shared library."""
 
     def __init__(self, path: str = LIBRARY):
-        if not os.path.exists(path):
+        if not os.path.exists(path) or (path == LIBRARY and
+                                        os.path.getmtime(SOURCE) > os.path.getmtime(path)):
             build(output=path)
         self.path = path
         lib = ctypes.CDLL(path)
@@ -95,6 +96,7 @@ class Oracle:
             "oracle_rotate_rows_f32": (i32, [vp, i64, i64, i32, vp]),
             "oracle_rotate_rows_f64": (i32, [vp, i64, i64, i32, vp]),
             "oracle_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i32]),
+            "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
             "oracle_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, i32]),
             "oracle_epilogue": (i32, [vp, i64, i64, vp, vp, vp, f32, i32, vp, i64, i32]),
             "oracle_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
@@ -141,6 +143,22 @@ class Oracle:
                                            _p(raw), threads)
         self._check(rc, "quantize_rows")
         return Packed(raw, M, K)
+
+    def modulate_rows(self, X: np.ndarray, scale: np.ndarray, shift=None, K: int | None = None,
+                      threads: int = 1) -> np.ndarray:
+        """The Modulate producer on the first K columns of X: binary32 [M, K]."""
+        code = _dtype_code(X)
+        X = np.ascontiguousarray(X)
+        M, ldx = X.shape
+        K = ldx if K is None else K
+        sc = np.ascontiguousarray(scale, dtype=np.float32)
+        sh = None if shift is None else np.ascontiguousarray(shift, dtype=np.float32)
+        assert sc.shape == (K,) and (sh is None or sh.shape == (K,))
+        Y = np.empty((M, K), dtype=np.float32)
+        rc = self.lib.oracle_modulate_rows(_p(X), code, M, K, ldx, _p(sc),
+                                           None if sh is None else _p(sh), _p(Y), threads)
+        self._check(rc, "modulate_rows")
+        return Y
 
     def weight_prep(self, W: np.ndarray, G: int, threads: int = 1):
         """Offline weight rotation + per-output-row quantization -> (Q_w, s_w)."""

@@ -30,6 +30,12 @@
  *     multiple of 4, pad rows zero) followed by float [M_pad] (pad zero).
  *   - the per-linear input scale alpha pre-multiplies the activation (one
  *     rounding) and divides the output after the weight scale, before bias.
+ *   - the Modulate producer (page "ggml operator extensions", section
+ *     "sd.cpp integration", the Modulate operator and its ConvRot fusion) is
+ *     applied to the widened binary32 input with per-channel vectors of
+ *     length K shared by every row: (x + x * scale) + shift, three separately
+ *     rounded operations, the shift being optional.  Its binary32 output is
+ *     the input of the quantizer above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -237,6 +243,34 @@ int oracle_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64
         free(y);
     }
     return failed ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- producer */
+
+/*
+ * Modulate (page "ggml operator extensions", section "sd.cpp integration"):
+ * Y[r, i] = (x + x * scale[i]) + shift[i] with x = widen(X[r, i]); shift may
+ * be NULL (scale-only modulation).  Y is binary32 [M][K], contiguous.
+ */
+int oracle_modulate_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float *scale, const float *shift, float *Y, int threads)
+{
+    if (!X || !scale || !Y || M < 0 || K < 1 || ldx < K)
+        return ORACLE_EINVAL;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_EUNSUPPORTED;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t r = 0; r < M; ++r) {
+        for (int64_t i = 0; i < K; ++i) {
+            const float x = load_widened(X, x_dtype, r * ldx + i);
+            const float xs = x * scale[i];
+            float y = x + xs;
+            if (shift)
+                y = y + shift[i];
+            Y[r * K + i] = y;
+        }
+    }
+    return ORACLE_OK;
 }
 
 /* ------------------------------------------------------------- contraction */

@@ -380,4 +380,45 @@ def pin_rotation_reduces_error(o):
     assert errs[256] < 0.7 * errs[1], errs
 
 
+def pin_modulate_exact(o):
+    """The Modulate producer against exact rational arithmetic with binary32
+    rounding at each step: fl(fl(x + fl(x * scale)) + shift), the vectors
+    indexed by column (page "ggml operator extensions", the Modulate
+    operator); with and without the shift, for binary32 and bf16 rows."""
+    rng = np.random.default_rng(41)
+    M, K = 3, 64
+    X = workloads.gaussian_activations(rng, M, K, 0.05, 20.0, workloads.F32)
+    sc = (rng.standard_normal(K) * 0.7).astype(np.float32)
+    sh = (rng.standard_normal(K) * 0.7).astype(np.float32)
+    Xb = workloads.f32_to_bf16_bits(X)
+    for src, xw in ((X, X), (Xb, workloads.bf16_bits_to_f32(Xb))):
+        for shift in (sh, None):
+            Y = o.modulate_rows(src, sc, shift)
+            for r in range(M):
+                for i in range(K):
+                    x = F(xw[r, i])
+                    t = rne_f32(x + rne_f32(x * F(sc[i])))
+                    if shift is not None:
+                        t = rne_f32(t + F(shift[i]))
+                    assert F(Y[r, i]) == t, f"modulate ({r},{i}) shift={shift is not None}"
+
+
+def pin_modulate_special_cases(o):
+    """scale = 0 without shift is the identity; scale = 1 doubles exactly, so the
+    quantizer's codes are unchanged and its scales double; a row stride is
+    honoured (only the first K columns are read)."""
+    rng = np.random.default_rng(42)
+    M, K, G = 6, 512, 64
+    wide = workloads.gaussian_activations(rng, M, K + 32, 0.01, 20.0, workloads.F32)
+    X = np.ascontiguousarray(wide[:, :K])
+    zero = np.zeros(K, np.float32)
+    assert np.array_equal(o.modulate_rows(X, zero).view(np.uint32), X.view(np.uint32))
+    two = o.modulate_rows(X, np.ones(K, np.float32))
+    assert np.array_equal(two, 2 * X)
+    p1, p2 = o.quantize_rows(X, G), o.quantize_rows(two, G)
+    assert np.array_equal(p1.q, p2.q) and np.array_equal(p2.s, 2 * p1.s)
+    sc = (rng.standard_normal(K) * 0.3).astype(np.float32)
+    assert np.array_equal(o.modulate_rows(wide, sc, K=K), o.modulate_rows(X, sc))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

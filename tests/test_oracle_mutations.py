@@ -47,6 +47,11 @@ MUTATIONS = {
     "bf16_widen": ("uint32_t u = (uint32_t)((const uint16_t *)X)[idx] << 16;",
                    "uint32_t u = (uint32_t)((const uint16_t *)X)[idx] << 15;"),
     "bf16_round_half_up": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "modulate_folded": ("const float xs = x * scale[i];\n            float y = x + xs;",
+                        "const float xs = 1.0f + scale[i];\n            float y = x * xs;"),
+    "modulate_shift_first": ("float y = x + xs;\n            if (shift)\n                y = y + shift[i];",
+                             "float y = x;\n            if (shift)\n                y = y + shift[i];\n            y = y + xs;"),
+    "modulate_scale_index": ("const float xs = x * scale[i];", "const float xs = x * scale[K - 1 - i];"),
     "zero_row_scale": ("        *s_out = 0.0f;\n        memset(q, 0, (size_t)K);\n        return;",
                        "        m = 1.0f;"),
 }
