@@ -52,10 +52,12 @@ def source_hash(path: str) -> str:
 
 
 def quantize_bytes(w: workloads.Workload) -> int:
-    """Algorithmic bytes of one quantize pass: read X once, write the packed tensor."""
+    """Algorithmic bytes of one quantize pass: read X once (and the Modulate
+    producer's two per-channel vectors, if any), write the packed tensor."""
     esz = 2 if w.x_dtype == workloads.BF16 else 4
     m_pad = (w.M + 3) // 4 * 4
-    return w.M * w.K * esz + m_pad * w.K + 4 * m_pad
+    mod = 8 * w.K if w.modulate else 0
+    return w.M * w.K * esz + m_pad * w.K + 4 * m_pad + mod
 
 
 def gemm_ops(w: workloads.Workload, n_linears: int) -> int:
@@ -150,11 +152,14 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
     X = np.ascontiguousarray(inp.X[:rows])
     t0 = time.perf_counter()
+    if w.modulate:
+        X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
     o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
     dt = time.perf_counter() - t0
     ops = 2 * rows * w.N * w.K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.M} rows of {w.name} (quantize + int32 GEMM + reconstruction "
+            "sample": f"{rows} of {w.M} rows of {w.name} ({'modulate + ' if w.modulate else ''}"
+                      f"quantize + int32 GEMM + reconstruction "
                       f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
 
 
@@ -224,9 +229,15 @@ def main() -> int:
                           device=dev) for _ in range(w.n_linears)]
         sets.append((Xd, ws, Ys))
 
+    mod = (cr.Modulate(torch.from_numpy(inp.mod_scale).to(dev), torch.from_numpy(inp.mod_shift).to(dev))
+           if w.modulate else None)
+
     def quantize(i):
         Xd, ws, Ys = sets[i % n_sets]
-        cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
+        if mod is not None:
+            cr.convrot_quantize_rows_pre(Xd, mod, w.G, lins[0]["input_scale"], packed=ws)
+        else:
+            cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
 
     def gemm(i):
         Xd, ws, Ys = sets[i % n_sets]
@@ -237,8 +248,8 @@ def main() -> int:
     def step(i):
         if shared:
             Xd, ws, Ys = sets[i % n_sets]
-            cr.convrot_int8_linear_shared(
-                Xd, w.G, [dict(l, Y=Y) for l, Y in zip(lins, Ys)], workspace=ws)
+            cr.convrot_int8_linear_shared_pre(
+                Xd, mod, w.G, [dict(l, Y=Y) for l, Y in zip(lins, Ys)], workspace=ws)
         else:
             quantize(i)
             gemm(i)
@@ -290,7 +301,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W i8 [{w.N},{w.K}] x "
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
-                               f"{list(w.input_scales)}",
+                               f"{list(w.input_scales)}"
+                               + (", Modulate producer fused" if w.modulate else ""),
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,
                    "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets},
         "step_us_events": round(ev_step_us, 3),

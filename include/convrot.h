@@ -146,6 +146,43 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
                                int group_size, int n, const convrot_linear_desc *descs,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* A producer fused into the quantization pass: applied to each widened input
+ * element before the input scale and the rotation, so that the producer's
+ * output never goes to memory.
+ *
+ * CONVROT_PRE_MODULATE (page "ggml operator extensions", section "sd.cpp
+ * integration": the Modulate operator and its fusion with ConvRot, which takes
+ * contiguous per-channel parameters):
+ *     x' = (x + x * scale[i]) + shift[i]       i = input feature (column)
+ * three separately rounded binary32 operations; shift may be NULL (scale-only
+ * modulation, no add).  scale and shift are device vectors of K floats shared
+ * by every row, 16-byte aligned. */
+typedef enum { CONVROT_PRE_NONE = 0, CONVROT_PRE_MODULATE = 1 } convrot_pre_kind;
+
+typedef struct {
+    int kind;             /* convrot_pre_kind */
+    const float *scale;   /* MODULATE: [K] (device), required */
+    const float *shift;   /* MODULATE: [K] (device) or NULL */
+} convrot_pre;
+
+/* convrot_quantize_rows with a producer.  pre may be NULL or of kind
+ * CONVROT_PRE_NONE (then identical to convrot_quantize_rows).  CONVROT_EINVAL
+ * for a MODULATE descriptor without scale or with misaligned vectors,
+ * CONVROT_EUNSUPPORTED for an unknown kind, CONVROT_EOVERLAP if packed
+ * overlaps X, scale or shift. */
+int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const convrot_pre *pre, int group_size, float input_scale,
+                              void *packed, void *stream);
+
+/* convrot_int8_linear_shared with a producer applied in every quantization
+ * pass (same rules for pre as above).  The workspace must not overlap scale or
+ * shift; an output may alias them (they are consumed before any output is
+ * written), like X. */
+int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const convrot_pre *pre, int group_size, int n,
+                                   const convrot_linear_desc *descs, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* The raw int32 accumulator A = Q_x Q_w^T (same contraction kernel as
  * int8_linear, with the reconstruction replaced by an int32 store); for
  * checking the contraction bit for bit.  A is [M][N] int32. */

@@ -16,6 +16,7 @@ LIBRARY = os.path.join(_HERE, "libconvrot.so")
 
 OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
+PRE_NONE, PRE_MODULATE = 0, 1
 MAX_LINEARS = 16
 
 _lib = None
@@ -41,6 +42,32 @@ class LinearDesc(ctypes.Structure):
     ]
 
 
+class PreDesc(ctypes.Structure):
+    """Mirror of convrot_pre."""
+    _fields_ = [
+        ("kind", ctypes.c_int),
+        ("scale", ctypes.c_void_p),
+        ("shift", ctypes.c_void_p),
+    ]
+
+
+class Modulate:
+    """The Modulate producer (x + x * scale) + shift with per-channel float32
+    device vectors of K elements; shift may be None."""
+
+    def __init__(self, scale, shift=None):
+        self.scale = scale
+        self.shift = shift
+
+    def desc(self) -> PreDesc:
+        return PreDesc(PRE_MODULATE, self.scale.data_ptr(),
+                       None if self.shift is None else self.shift.data_ptr())
+
+
+def _pre(pre):
+    return None if pre is None else ctypes.byref(pre.desc())
+
+
 def library(path: str = LIBRARY) -> ctypes.CDLL:
     """Load libconvrot.so (raises if it has not been built)."""
     global _lib
@@ -54,12 +81,16 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
     sigs = {
         "convrot_packed_bytes": (sz, [i64, i64]),
         "convrot_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp]),
+        "convrot_quantize_rows_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc), i32,
+                                            f32, vp, vp]),
         "int8_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
         "convrot_workspace_bytes": (sz, [i64, i64, i32]),
         "convrot_int8_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
                                       i64, vp, sz, vp]),
         "convrot_int8_linear_shared": (i32, [vp, i32, i64, i64, i64, i32, i32,
                                              ctypes.POINTER(LinearDesc), vp, sz, vp]),
+        "convrot_int8_linear_shared_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc),
+                                                 i32, i32, ctypes.POINTER(LinearDesc), vp, sz, vp]),
         "convrot_int8_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "convrot_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -158,6 +189,23 @@ def convrot_quantize_rows(X, group_size: int, input_scale: float = 1.0, packed=N
     return packed
 
 
+def convrot_quantize_rows_pre(X, pre, group_size: int, input_scale: float = 1.0, packed=None,
+                              K: int | None = None, stream=None):
+    """convrot_quantize_rows with a producer (a Modulate, or None) applied to
+    each element before the input scale and the rotation."""
+    torch = _torch()
+    M = X.shape[0]
+    ldx = _row_stride(X) if M > 0 else X.shape[1]
+    K = X.shape[1] if K is None else K
+    if packed is None:
+        packed = torch.empty(convrot_packed_bytes(M, K), dtype=torch.uint8, device=X.device)
+    rc = library().convrot_quantize_rows_pre(_ptr(X), _dtype_code(X), M, K, ldx, _pre(pre),
+                                             group_size, ctypes.c_float(input_scale), _ptr(packed),
+                                             _stream(stream, X))
+    _check("convrot_quantize_rows_pre", rc)
+    return packed
+
+
 def int8_linear(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, Y=None,
                 y_dtype: int = F32, M: int | None = None, stream=None):
     """Y = reconstruction of Q_x Q_w^T (Qx [M, K] int8 rows, s_x [M])."""
@@ -207,9 +255,7 @@ def convrot_int8_linear(X, group_size: int, input_scale: float, Qw, s_w=None, bi
     return Y
 
 
-def convrot_int8_linear_shared(X, group_size: int, linears, workspace=None, stream=None):
-    """``linears``: sequence of dicts with keys Qw, s_w, bias, input_scale and
-    optionally Y / y_dtype.  Returns the list of outputs."""
+def _shared(X, group_size: int, linears, workspace, stream, pre):
     torch = _torch()
     M, K = X.shape
     ldx = _row_stride(X) if M > 0 else K
@@ -238,8 +284,28 @@ def convrot_int8_linear_shared(X, group_size: int, linears, workspace=None, stre
     if workspace is None:
         workspace = torch.empty(max(convrot_workspace_bytes(M, K, len(scales)), 1),
                                 dtype=torch.uint8, device=X.device)
-    rc = library().convrot_int8_linear_shared(_ptr(X), _dtype_code(X), M, K, ldx, group_size, n,
-                                              descs, _ptr(workspace), workspace.numel(),
-                                              _stream(stream, X))
-    _check("convrot_int8_linear_shared", rc)
+    if pre is None:
+        rc = library().convrot_int8_linear_shared(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
+                                                  n, descs, _ptr(workspace), workspace.numel(),
+                                                  _stream(stream, X))
+        _check("convrot_int8_linear_shared", rc)
+    else:
+        rc = library().convrot_int8_linear_shared_pre(_ptr(X), _dtype_code(X), M, K, ldx,
+                                                      _pre(pre), group_size, n, descs,
+                                                      _ptr(workspace), workspace.numel(),
+                                                      _stream(stream, X))
+        _check("convrot_int8_linear_shared_pre", rc)
     return outs
+
+
+def convrot_int8_linear_shared(X, group_size: int, linears, workspace=None, stream=None):
+    """``linears``: sequence of dicts with keys Qw, s_w, bias, input_scale and
+    optionally Y / y_dtype.  Returns the list of outputs."""
+    return _shared(X, group_size, linears, workspace, stream, None)
+
+
+def convrot_int8_linear_shared_pre(X, pre, group_size: int, linears, workspace=None,
+                                   stream=None):
+    """convrot_int8_linear_shared with a producer (a Modulate) applied in every
+    quantization pass."""
+    return _shared(X, group_size, linears, workspace, stream, pre)

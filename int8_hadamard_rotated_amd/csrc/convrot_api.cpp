@@ -151,6 +151,26 @@ GemmLinear make_linear(const int8_t *Qw, const float *s_w, const float *bias, in
 
 int out_kind_of(int y_dtype) { return y_dtype == CONVROT_BF16 ? kOutBF16 : kOutF32; }
 
+// Validates a producer descriptor (nullable) and returns the spans it reads.
+int check_pre(const convrot_pre *pre, int64_t K, PreOp *op, Span *s_scale, Span *s_shift)
+{
+    *op = PreOp{};
+    *s_scale = Span{};
+    *s_shift = Span{};
+    if (!pre || pre->kind == CONVROT_PRE_NONE)
+        return CONVROT_OK;
+    if (pre->kind != CONVROT_PRE_MODULATE)
+        return CONVROT_EUNSUPPORTED;
+    if (!pre->scale || !aligned(pre->scale, 16) || (pre->shift && !aligned(pre->shift, 16)))
+        return CONVROT_EINVAL;
+    op->kind = kPreModulate;
+    op->scale = pre->scale;
+    op->shift = pre->shift;
+    *s_scale = span_of(pre->scale, 4 * K);
+    *s_shift = span_of(pre->shift, 4 * K);
+    return CONVROT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,22 +190,36 @@ size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed)
     return (size_t)n_packed * (size_t)round_up((int64_t)convrot_packed_bytes(M, K), 256);
 }
 
-int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                          int group_size, float input_scale, void *packed, void *stream)
+int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const convrot_pre *pre, int group_size, float input_scale,
+                              void *packed, void *stream)
 {
     int rc = check_quantize_args(X, x_dtype, M, K, ldx, group_size, input_scale);
+    if (rc != CONVROT_OK)
+        return rc;
+    PreOp op;
+    Span sc, sh;
+    rc = check_pre(pre, K, &op, &sc, &sh);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0)
         return CONVROT_OK;
     if (!packed || !aligned(packed, 16))
         return CONVROT_EINVAL;
-    if (overlap(rows_span(X, M, K, ldx, elem_bytes(x_dtype)),
-                span_of(packed, (int64_t)convrot_packed_bytes(M, K))))
+    const Span out = span_of(packed, (int64_t)convrot_packed_bytes(M, K));
+    if (overlap(rows_span(X, M, K, ldx, elem_bytes(x_dtype)), out) || overlap(sc, out) ||
+        overlap(sh, out))
         return CONVROT_EOVERLAP;
     (void)hipGetLastError();
-    return hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, input_scale, packed,
+    return hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, input_scale, op, packed,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          int group_size, float input_scale, void *packed, void *stream)
+{
+    return convrot_quantize_rows_pre(X, x_dtype, M, K, ldx, nullptr, group_size, input_scale,
+                                     packed, stream);
 }
 
 int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
@@ -250,13 +284,19 @@ int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t
     return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
-int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                               int group_size, int n, const convrot_linear_desc *descs,
-                               void *workspace, size_t workspace_bytes, void *stream)
+int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const convrot_pre *pre, int group_size, int n,
+                                   const convrot_linear_desc *descs, void *workspace,
+                                   size_t workspace_bytes, void *stream)
 {
     if (n < 1 || n > kMaxLinears || !descs)
         return CONVROT_EINVAL;
     int rc = check_quantize_args(X, x_dtype, M, K, ldx, group_size, 1.0f);
+    if (rc != CONVROT_OK)
+        return rc;
+    PreOp op;
+    Span sc, sh;
+    rc = check_pre(pre, K, &op, &sc, &sh);
     if (rc != CONVROT_OK)
         return rc;
     rc = check_contraction_k(K);
@@ -291,7 +331,7 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
         return CONVROT_EINVAL;
     const Span ws = span_of(workspace, slot_bytes * n_slots);
     const Span xs = rows_span(X, M, K, ldx, elem_bytes(x_dtype));
-    if (overlap(ws, xs))
+    if (overlap(ws, xs) || overlap(ws, sc) || overlap(ws, sh))
         return CONVROT_EOVERLAP;
     for (int i = 0; i < n; ++i) {
         if (overlap(chk[i].y, ws) || overlap(chk[i].qw, ws) || overlap(chk[i].sw, ws) ||
@@ -309,7 +349,7 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
     (void)hipGetLastError();
     int8_t *base = static_cast<int8_t *>(workspace);
     for (int s = 0; s < n_slots; ++s) {
-        rc = hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, scales[s],
+        rc = hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, scales[s], op,
                                         base + s * slot_bytes, st));
         if (rc != CONVROT_OK)
             return rc;
@@ -336,6 +376,14 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
             return rc;
     }
     return CONVROT_OK;
+}
+
+int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               int group_size, int n, const convrot_linear_desc *descs,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return convrot_int8_linear_shared_pre(X, x_dtype, M, K, ldx, nullptr, group_size, n, descs,
+                                          workspace, workspace_bytes, stream);
 }
 
 int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -12,10 +12,19 @@ namespace convrot_detail {
 // workgroup per group of rows, at most 256 quads of 4 lanes per row.
 int64_t quantize_max_k(int64_t K);
 
-// Launch the rotate + row-max + quantize + pack kernel.  Arguments are
-// already validated (see convrot_quantize_rows).
+// Producer applied to each widened input element before the rotation.
+enum PreKind : int { kPreNone = 0, kPreModulate = 1 };
+
+struct PreOp {
+    int kind = kPreNone;
+    const float *scale = nullptr;   // kPreModulate: per-channel [K], 16-byte aligned
+    const float *shift = nullptr;   // kPreModulate: per-channel [K] or null
+};
+
+// Launch the (producer +) rotate + row-max + quantize + pack kernel.
+// Arguments are already validated (see convrot_quantize_rows_pre).
 hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
-                           float alpha, void *packed, hipStream_t stream);
+                           float alpha, const PreOp &pre, void *packed, hipStream_t stream);
 
 // ------------------------------------------------------------------- GEMM
 constexpr int kMaxLinears = 16;

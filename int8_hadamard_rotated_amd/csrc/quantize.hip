@@ -2,7 +2,12 @@
 //
 // Computes, per activation row (page "INT8 Convrot Safetensors", section
 // "How INT8 convrot works", subsection "Runtime activation quantization"):
-//   x  = widen(X[r, :]) * alpha            (multiply only when alpha != 1)
+//   x  = widen(X[r, :])
+//   x  = (x + x * scale) + shift           (optional Modulate producer: page
+//                                           "ggml operator extensions", section
+//                                           "sd.cpp integration"; per-channel
+//                                           vectors, shift optional)
+//   x  = x * alpha                         (multiply only when alpha != 1)
 //   y  = x R_G per contiguous G-group       (R_G = H4^(x)n, G = 4^n)
 //   m  = max |y| over the whole row
 //   s  = fl(m / 127)  and  q = rne(fl(y * fl(127 / m)))  (m = 0: s = 0, q = 0)
@@ -117,9 +122,36 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
     return lo | hi;
 }
 
-template <typename XT, int G, int NC, bool SCALED>
+// The Modulate producer on one chunk of 8 elements whose first column is
+// `col`: x = (x + x * scale) + shift, each operation rounded on its own (the
+// file is compiled without contraction).  MOD: 1 scale only, 2 with shift.
+// The vectors are read through the caches: every row reads the same ones.
+template <int MOD>
+__device__ __forceinline__ void modulate8(float (&v)[8], const float *__restrict__ scale,
+                                          const float *__restrict__ shift, int64_t col)
+{
+    if constexpr (MOD != 0) {
+        const v4f s0 = *reinterpret_cast<const v4f *>(scale + col);
+        const v4f s1 = *reinterpret_cast<const v4f *>(scale + col + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            v[p] = v[p] + v[p] * sc[p];
+        if constexpr (MOD == 2) {
+            const v4f h0 = *reinterpret_cast<const v4f *>(shift + col);
+            const v4f h1 = *reinterpret_cast<const v4f *>(shift + col + 4);
+            const float sh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                v[p] = v[p] + sh[p];
+        }
+    }
+}
+
+template <typename XT, int G, int NC, bool SCALED, int MOD>
 __global__ __launch_bounds__(1024) void quantize_rows_kernel(
     const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
+    const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
     int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
@@ -147,6 +179,9 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             load8(xr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1), v[c]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            modulate8<MOD>(v[c], mod_scale, mod_shift, span0 + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1));
 
         if constexpr (SCALED) {
 #pragma unroll
@@ -245,9 +280,10 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
 // region needs no barrier.  Odd quads store their pieces with the slot index
 // XOR-ed by one (codes: by 4 * (quad % 4)) so that the lanes of one read
 // instruction spread over distinct LDS banks.
-template <int G, int NC, bool SCALED>
+template <int G, int NC, bool SCALED, int MOD>
 __global__ __launch_bounds__(256) void quantize_rows_staged(
     const float *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
+    const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
     int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
@@ -319,6 +355,10 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
                     v[c][4 * h + t] = __builtin_bit_cast(float, w[t]);
             }
         }
+        const int64_t span_me = (int64_t)q_in_row * (32 * NC);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            modulate8<MOD>(v[c], mod_scale, mod_shift, span_me + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1));
 
         if constexpr (SCALED) {
 #pragma unroll
@@ -419,19 +459,19 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
 template <int NC>
 constexpr size_t kStagedWaveBytes = 16 * 32 * NC * 4;
 
-template <int G, int NC>
-void launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alpha, int8_t *Q,
-                   float *S, int64_t m_pad, int qr, int rows, hipStream_t stream)
+template <int G, int NC, int MOD>
+void launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
+                   int8_t *Q, float *S, int64_t m_pad, int qr, int rows, hipStream_t stream)
 {
     const int threads = 4 * qr * rows;
     const size_t lds = (size_t)((threads + 63) / 64) * kStagedWaveBytes<NC>;
     const int64_t blocks = (m_pad + rows - 1) / rows;
     if (alpha != 1.0f)
-        hipLaunchKernelGGL((quantize_rows_staged<G, NC, true>), dim3((unsigned)blocks), dim3(threads), lds,
-                           stream, X, M, m_pad, K, ldx, alpha, Q, S, qr, rows);
+        hipLaunchKernelGGL((quantize_rows_staged<G, NC, true, MOD>), dim3((unsigned)blocks), dim3(threads), lds,
+                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows);
     else
-        hipLaunchKernelGGL((quantize_rows_staged<G, NC, false>), dim3((unsigned)blocks), dim3(threads), lds,
-                           stream, X, M, m_pad, K, ldx, alpha, Q, S, qr, rows);
+        hipLaunchKernelGGL((quantize_rows_staged<G, NC, false, MOD>), dim3((unsigned)blocks), dim3(threads), lds,
+                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows);
 }
 
 int gcd_int(int a, int b)
@@ -444,9 +484,9 @@ int gcd_int(int a, int b)
     return a;
 }
 
-template <typename XT, int G, int NC>
-void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, void *packed,
-                  hipStream_t stream)
+template <typename XT, int G, int NC, int MOD>
+void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
+                  void *packed, hipStream_t stream)
 {
     const int64_t m_pad = (M + 3) / 4 * 4;
     const int qr = (int)(K / (32 * NC));
@@ -463,44 +503,56 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
     if constexpr (sizeof(XT) == 4) {
         // binary32 rows of up to 256 threads per workgroup take the staged kernel
         if (threads <= 256)
-            return launch_staged<G, NC>(static_cast<const float *>(X), M, K, ldx, alpha, Q, S, m_pad,
-                                        qr, rows, stream);
+            return launch_staged<G, NC, MOD>(static_cast<const float *>(X), M, K, ldx, alpha, pre, Q,
+                                             S, m_pad, qr, rows, stream);
     }
     if (alpha != 1.0f)
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, Q, S, qr, rows);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, Q, S, qr, rows);
 }
 
-template <typename XT, int NC>
-void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, void *packed,
-               hipStream_t stream)
+template <typename XT, int NC, int MOD>
+void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+               const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
-    case 4: launch_typed<XT, 4, NC>(X, M, K, ldx, alpha, packed, stream); break;
-    case 16: launch_typed<XT, 16, NC>(X, M, K, ldx, alpha, packed, stream); break;
-    case 64: launch_typed<XT, 64, NC>(X, M, K, ldx, alpha, packed, stream); break;
+    case 4: launch_typed<XT, 4, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 16: launch_typed<XT, 16, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 64: launch_typed<XT, 64, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
     default:
         if constexpr (NC == 8)
-            launch_typed<XT, 256, 8>(X, M, K, ldx, alpha, packed, stream);
+            launch_typed<XT, 256, 8, MOD>(X, M, K, ldx, alpha, pre, packed, stream);
         break;
     }
 }
 
-template <typename XT>
+template <typename XT, int MOD>
 void launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
-                  void *packed, hipStream_t stream)
+                  const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (K % 256 == 0)
-        launch_nc<XT, 8>(G, X, M, K, ldx, alpha, packed, stream);
+        launch_nc<XT, 8, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else if (K % 128 == 0)
-        launch_nc<XT, 4>(G, X, M, K, ldx, alpha, packed, stream);
+        launch_nc<XT, 4, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_nc<XT, 2>(G, X, M, K, ldx, alpha, packed, stream);
+        launch_nc<XT, 2, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
+}
+
+template <typename XT>
+void launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                const PreOp &pre, void *packed, hipStream_t stream)
+{
+    if (pre.kind == kPreModulate && pre.shift)
+        launch_dtype<XT, 2>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else if (pre.kind == kPreModulate)
+        launch_dtype<XT, 1>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else
+        launch_dtype<XT, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 }  // namespace
@@ -516,12 +568,12 @@ int64_t quantize_max_k(int64_t K)
 }
 
 hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
-                           float alpha, void *packed, hipStream_t stream)
+                           float alpha, const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (x_dtype == 0)
-        launch_dtype<float>(G, X, M, K, ldx, alpha, packed, stream);
+        launch_pre<float>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_dtype<uint16_t>(G, X, M, K, ldx, alpha, packed, stream);
+        launch_pre<uint16_t>(G, X, M, K, ldx, alpha, pre, packed, stream);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     assert header_functions() == sorted([
         "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
-        "convrot_status_string"])
+        "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -93,6 +93,34 @@ def test_quantize_validation(lib):
     assert q(lib, packed=BASE + 1024) == EOVL            # packed overlaps X
     assert q(lib, M=0) == OK                             # empty input: nothing enqueued
     assert q(lib, M=0, X=0, packed=0) == OK
+
+
+def qpre(lib, kind=cr.PRE_MODULATE, sc=BASE + 96 * MB, sh=BASE + 97 * MB, M=8, K=256,
+         packed=BASE + 64 * MB, raw=False):
+    d = None if raw else ctypes.byref(cr.PreDesc(kind, sc, sh))
+    return lib.convrot_quantize_rows_pre(ctypes.c_void_p(BASE), cr.F32, M, K, K, d, 16,
+                                         ctypes.c_float(1.0), ctypes.c_void_p(packed), None)
+
+
+def test_producer_validation(lib):
+    assert qpre(lib, kind=7) == EUNSUP
+    assert qpre(lib, sc=0) == EINVAL                     # modulation needs its scale
+    assert qpre(lib, sc=BASE + 96 * MB + 4) == EINVAL    # 16-byte aligned vectors
+    assert qpre(lib, sh=BASE + 97 * MB + 8) == EINVAL
+    assert qpre(lib, sc=BASE + 64 * MB + 512) == EOVL    # packed overlaps the scale
+    assert qpre(lib, sh=BASE + 64 * MB + 2048) == EOVL   # ... or the shift
+    assert qpre(lib, M=0) == OK
+    assert qpre(lib, M=0, raw=True) == OK                # NULL producer
+    assert qpre(lib, kind=cr.PRE_NONE, sc=0, sh=0, M=0) == OK
+    # the shared entry: the workspace must not overlap the vectors
+    d = cr.LinearDesc(BASE + 16 * MB, None, None, 32, 1.0, BASE + 32 * MB, cr.F32, 32)
+    pre = cr.PreDesc(cr.PRE_MODULATE, BASE + 48 * MB + 256, None)
+    f = lib.convrot_int8_linear_shared_pre
+    assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),
+             ctypes.c_void_p(BASE + 48 * MB), MB, None) == EOVL
+    pre.kind = 9
+    assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),
+             ctypes.c_void_p(BASE + 48 * MB), MB, None) == EUNSUP
 
 
 def lin(lib, Qx=BASE, sx=BASE + 8 * MB, M=8, K=256, Qw=BASE + 16 * MB, sw=BASE + 24 * MB,

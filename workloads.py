@@ -21,6 +21,10 @@ Recipe, per workload (fixed draw order):
     for each linear j:
         W_j = rng.standard_normal((N, K), float32) * 0.02
         b_j = rng.standard_normal(N, float32) * 0.1
+    when the workload has a Modulate producer (per-channel vectors, as the
+    adaLN modulation of a DiT block supplies them):
+        scale = rng.standard_normal(K, float32) * 0.3
+        shift = rng.standard_normal(K, float32) * 0.3
 """
 from __future__ import annotations
 
@@ -45,6 +49,7 @@ class Workload:
     seed: int = 0
     outlier_p: float = 0.005
     outlier_f: float = 30.0
+    modulate: bool = False            # a Modulate producer before the rotation
     note: str = ""
 
     @property
@@ -62,6 +67,9 @@ WORKLOADS = {
                        note="DiT MLP up-projection, bf16 in/out"),
     "qkv": Workload("qkv", 4096, 3072, 3072, 256, F32, F32, (1.0, 1.0, 1.0, 0.5), seed=3,
                     note="three linears sharing one packed input, plus one at input scale 0.5"),
+    "mlp_up_mod": Workload("mlp_up_mod", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=5,
+                           modulate=True,
+                           note="DiT MLP up-projection with its Modulate producer fused"),
     "mlp_down": Workload("mlp_down", 16384, 12288, 3072, 256, BF16, BF16, (1.0,), seed=4,
                          note="batched MLP down-projection, 4 images x 4096 tokens, bf16 in/out"),
 }
@@ -109,6 +117,8 @@ class Inputs:
     X: np.ndarray                      # float32 or uint16 (bf16 bits), [M,K]
     W: list = field(default_factory=list)   # float32 [N,K] per linear
     b: list = field(default_factory=list)   # float32 [N] per linear
+    mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
+    mod_shift: np.ndarray | None = None     # float32 [K]
 
 
 def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> Inputs:
@@ -124,7 +134,16 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
         W, b = gaussian_weights(rng, w.N, w.K)
         inp.W.append(W)
         inp.b.append(b)
+    if w.modulate:
+        inp.mod_scale, inp.mod_shift = modulation(rng, w.K)
     return inp
+
+
+def modulation(rng: np.random.Generator, K: int, sigma: float = 0.3):
+    """Per-channel Modulate vectors (scale, shift), each N(0, sigma) fp32 [K]."""
+    sc = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
+    sh = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
+    return sc, sh
 
 
 def random_codes(rng: np.random.Generator, shape, lo: int = -127, hi: int = 127) -> np.ndarray:
