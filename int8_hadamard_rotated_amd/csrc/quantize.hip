@@ -122,6 +122,24 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
     return lo | hi;
 }
 
+// Workgroup quad index -> (row within the workgroup, quad within the row).
+// Without a producer quads are row-major.  With the Modulate producer they
+// are column-major, so that the quads of one wave that read the same columns
+// (of different rows) load the same per-channel parameters in one
+// instruction, which the memory pipeline serves once.
+template <int MOD>
+__device__ __forceinline__ void quad_place(int quad, int quads_per_row, int rows_per_wg, int &row,
+                                           int &q_in_row)
+{
+    if constexpr (MOD != 0) {
+        row = quad % rows_per_wg;
+        q_in_row = quad / rows_per_wg;
+    } else {
+        row = quad / quads_per_row;
+        q_in_row = quad - row * quads_per_row;
+    }
+}
+
 // The Modulate producer on one chunk of 8 elements whose first column is
 // `col`: x = (x + x * scale) + shift, each operation rounded on its own (the
 // file is compiled without contraction).  MOD: 1 scale only, 2 with shift.
@@ -161,8 +179,8 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
     const int tid = threadIdx.x;
     const int quad = tid >> 2;
     const int j0 = tid & 1, j1 = (tid >> 1) & 1;
-    const int row_local = quad / quads_per_row;
-    const int q_in_row = quad - row_local * quads_per_row;
+    int row_local, q_in_row;
+    quad_place<MOD>(quad, quads_per_row, rows_per_wg, row_local, q_in_row);
     const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
     const int64_t span0 = (int64_t)q_in_row * (32 * NC);
     // A quad never straddles rows, so this branch is uniform per quad and the
@@ -301,8 +319,8 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     const int quad = tid >> 2;
     const int j0 = tid & 1, j1 = (tid >> 1) & 1;
     const int n_quads = quads_per_row * rows_per_wg;
-    const int row_local = quad / quads_per_row;
-    const int q_in_row = quad - row_local * quads_per_row;
+    int row_local, q_in_row;
+    quad_place<MOD>(quad, quads_per_row, rows_per_wg, row_local, q_in_row);
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     const int64_t row = row0 + row_local;
     const bool live = row < M;
@@ -319,10 +337,10 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     for (int i = 0; i < kLoadsPerLane; ++i) {
         const int p = 64 * i + lane;
         const int qw = 16 * wave + p / kQuadPieces;            // quad within the workgroup
-        const int rl = qw / quads_per_row;
+        int rl, qi;
+        quad_place<MOD>(qw, quads_per_row, rows_per_wg, rl, qi);
         const int64_t r = row0 + rl;
         if (qw < n_quads && r < M) {
-            const int qi = qw - rl * quads_per_row;
             const unsigned char *src = reinterpret_cast<const unsigned char *>(X + r * ldx + (int64_t)qi * (32 * NC)) +
                                        16 * (p % kQuadPieces);
             raw[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw *>(src));
@@ -445,10 +463,10 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
         const int p = 64 * i + lane;                            // wave code piece
         const int ql = p / kQuadOut, pi = p % kQuadOut;
         const int qw = 16 * wave + ql;
-        const int rl = qw / quads_per_row;
+        int rl, qi;
+        quad_place<MOD>(qw, quads_per_row, rows_per_wg, rl, qi);
         const int64_t r = row0 + rl;
         if (qw < n_quads && r < M_pad) {
-            const int qi = qw - rl * quads_per_row;
             const v4u val = *reinterpret_cast<const v4u *>(wst + 16 * (ql * kQuadOut + (pi ^ (4 * (ql & 3) % kQuadOut))));
             *reinterpret_cast<v4u *>(Q + r * K + (int64_t)qi * (32 * NC) + 16 * pi) = val;
         }
