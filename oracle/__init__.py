@@ -97,6 +97,7 @@ class Oracle:
             "oracle_rotate_rows_f64": (i32, [vp, i64, i64, i32, vp]),
             "oracle_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i32]),
             "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
+            "oracle_unpack_int4": (i32, [vp, i64, i64, vp]),
             "oracle_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, i32]),
             "oracle_epilogue": (i32, [vp, i64, i64, vp, vp, vp, f32, i32, vp, i64, i32]),
             "oracle_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
@@ -159,6 +160,15 @@ class Oracle:
                                            None if sh is None else _p(sh), _p(Y), threads)
         self._check(rc, "modulate_rows")
         return Y
+
+    def unpack_int4(self, W4: np.ndarray, K: int) -> np.ndarray:
+        """convrot_w4a4 packed weights [N, K/2] uint8 -> int8 [N, K]."""
+        W4 = np.ascontiguousarray(W4, dtype=np.uint8)
+        N = W4.shape[0]
+        assert W4.shape == (N, K // 2)
+        Qw = np.empty((N, K), dtype=np.int8)
+        self._check(self.lib.oracle_unpack_int4(_p(W4), N, K, _p(Qw)), "unpack_int4")
+        return Qw
 
     def weight_prep(self, W: np.ndarray, G: int, threads: int = 1):
         """Offline weight rotation + per-output-row quantization -> (Q_w, s_w)."""

@@ -30,6 +30,11 @@
  *     multiple of 4, pad rows zero) followed by float [M_pad] (pad zero).
  *   - the per-linear input scale alpha pre-multiplies the activation (one
  *     rounding) and divides the output after the weight scale, before bias.
+ *   - packed 4-bit weights (page "INT8 Convrot Safetensors", section
+ *     "Packed INT4 convrot", format convrot_w4a4): two signed 4-bit values per
+ *     byte, the low nibble holding the even input feature; they are decoded
+ *     to int8 and then take the same contraction and reconstruction as INT8
+ *     weights (the activations use the INT8 convrot quantization unchanged).
  *   - the Modulate producer (page "ggml operator extensions", section
  *     "sd.cpp integration", the Modulate operator and its ConvRot fusion) is
  *     applied to the widened binary32 input with per-channel vectors of
@@ -268,6 +273,28 @@ int oracle_modulate_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64
             if (shift)
                 y = y + shift[i];
             Y[r * K + i] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------- 4-bit weights */
+
+/*
+ * convrot_w4a4 weights (page "INT8 Convrot Safetensors", section "Packed INT4
+ * convrot"): W4 is [N][K/2] bytes; feature k of output o sits in byte
+ * o * K/2 + k/2, in the low nibble when k is even and the high nibble when k
+ * is odd, as a two's-complement 4-bit value (-8 .. 7).  Writes int8 [N][K].
+ */
+int oracle_unpack_int4(const uint8_t *W4, int64_t N, int64_t K, int8_t *Qw)
+{
+    if (!W4 || !Qw || N < 0 || K < 2 || K % 2 != 0)
+        return ORACLE_EINVAL;
+    for (int64_t o = 0; o < N; ++o) {
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t byte = W4[o * (K / 2) + k / 2];
+            const int nib = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+            Qw[o * K + k] = (int8_t)(nib >= 8 ? nib - 16 : nib);
         }
     }
     return ORACLE_OK;

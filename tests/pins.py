@@ -421,4 +421,45 @@ def pin_modulate_special_cases(o):
     assert np.array_equal(o.modulate_rows(wide, sc, K=K), o.modulate_rows(X, sc))
 
 
+def load_int4_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "int4_bytes.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                b, lo, hi = line.split()
+                rows.append((int(b, 16), int(lo), int(hi)))
+    return rows
+
+
+def pin_int4_golden(o):
+    """Packed 4-bit weights decode as the hand-written table says (low nibble is
+    the even feature; two's complement), at every position of a row."""
+    table = load_int4_golden()
+    K = 2 * len(table)
+    W4 = np.array([[b for b, _, _ in table], [b for b, _, _ in reversed(table)]], np.uint8)
+    Q = o.unpack_int4(W4, K)
+    want = [v for _, lo, hi in table for v in (lo, hi)]
+    assert Q[0].tolist() == want
+    assert Q[1].tolist() == [v for _, lo, hi in reversed(table) for v in (lo, hi)]
+
+
+def pin_int4_roundtrip(o):
+    """Decoding is a bijection from bytes onto pairs in [-8, 7]: re-encoding
+    every decoded pair (two's complement nibbles, even feature low) gives the
+    byte back, for all 256 bytes; and the contraction of decoded weights equals
+    integer loops over the table-decoded values."""
+    W4 = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    Q = o.unpack_int4(W4, 256)
+    assert Q.min() == -8 and Q.max() == 7
+    enc = ((Q[:, 0::2].astype(np.int64) & 15) | ((Q[:, 1::2].astype(np.int64) & 15) << 4))
+    assert np.array_equal(enc.astype(np.uint8), W4)
+    rng = np.random.default_rng(43)
+    Qx = workloads.random_codes(rng, (3, 256))
+    A = o.gemm_i32(Qx, Q)
+    for r in range(3):
+        for n in range(2):
+            assert int(A[r, n]) == sum(int(Qx[r, k]) * int(Q[n, k]) for k in range(256))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -52,6 +52,10 @@ MUTATIONS = {
     "modulate_shift_first": ("float y = x + xs;\n            if (shift)\n                y = y + shift[i];",
                              "float y = x;\n            if (shift)\n                y = y + shift[i];\n            y = y + xs;"),
     "modulate_scale_index": ("const float xs = x * scale[i];", "const float xs = x * scale[K - 1 - i];"),
+    "int4_high_nibble_first": ("const int nib = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                               "const int nib = (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    "int4_offset_binary": ("Qw[o * K + k] = (int8_t)(nib >= 8 ? nib - 16 : nib);",
+                           "Qw[o * K + k] = (int8_t)(nib - 8);"),
     "zero_row_scale": ("        *s_out = 0.0f;\n        memset(q, 0, (size_t)K);\n        return;",
                        "        m = 1.0f;"),
 }
