@@ -148,7 +148,10 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     o = oracle.get()
-    Qw, sw = o.weight_prep(inp.W[0], w.G, threads=threads)          # untimed
+    if w.w_bits == 4:                                                # untimed
+        Qw, sw = o.unpack_int4(inp.W[0], w.K), inp.s_w[0]
+    else:
+        Qw, sw = o.weight_prep(inp.W[0], w.G, threads=threads)
     yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
     X = np.ascontiguousarray(inp.X[:rows])
     t0 = time.perf_counter()
@@ -202,8 +205,13 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     # weights: rotated + quantized on the GPU by the library's own quantizer
+    # (4-bit weights are drawn already packed, with their scales)
     lins = []
-    for W, b, a in zip(inp.W, inp.b, w.input_scales):
+    for j, (W, b, a) in enumerate(zip(inp.W, inp.b, w.input_scales)):
+        if w.w_bits == 4:
+            lins.append(dict(Qw=torch.from_numpy(W).to(dev), s_w=torch.from_numpy(inp.s_w[j]).to(dev),
+                             bias=torch.from_numpy(b).to(dev), input_scale=a))
+            continue
         Wd = torch.from_numpy(W).to(dev)
         packed = cr.convrot_quantize_rows(Wd, w.G)
         Qw, sw = cr.packed_parts(packed, w.N, w.K)
@@ -243,7 +251,8 @@ def main() -> int:
         Xd, ws, Ys = sets[i % n_sets]
         l = lins[0]
         qx, sx = views[i % n_sets]
-        cr.int8_linear(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
+        lin_fn = cr.int4_linear if w.w_bits == 4 else cr.int8_linear
+        lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
 
     def step(i):
         if shared:
@@ -297,9 +306,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "i8" if w.w_bits == 8 else "i8 x i4",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W i8 [{w.N},{w.K}] x "
+        "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W {'i4' if w.w_bits == 4 else 'i8'} [{w.N},{w.K}] x "
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
                                f"{list(w.input_scales)}"
                                + (", Modulate producer fused" if w.modulate else ""),

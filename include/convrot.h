@@ -189,6 +189,24 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
 int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
                           int32_t *A, void *stream);
 
+/* 4-bit weights, format convrot_w4a4 (page "INT8 Convrot Safetensors",
+ * section "Packed INT4 convrot"): W4 is [N][K/2] bytes, feature k of output o
+ * in byte o*K/2 + k/2, low nibble for even k, high nibble for odd k, each a
+ * two's-complement value in -8..7; s_w is the F32 per-output weight scale.
+ * Activations are the INT8 convrot packed tensor as for int8_linear (the same
+ * packed tensor may feed INT8 and 4-bit linears).  Same reconstruction and
+ * conventions as int8_linear; W4 16-byte aligned; K % 64 == 0 and
+ * K <= 132096 (the contraction runs on 16 times the weights, exactly, in
+ * int32), else CONVROT_EUNSUPPORTED / CONVROT_EOVERFLOW. */
+int int4_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const uint8_t *W4,
+                const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
+                int y_dtype, int64_t ldy, void *stream);
+
+/* The raw int32 accumulator A = Q_x W^T for 4-bit weights W (same contraction
+ * kernel as int4_linear); A is [M][N] int32. */
+int convrot_int4_gemm_i32(const int8_t *Qx, const uint8_t *W4, int64_t M, int64_t K, int64_t N,
+                          int32_t *A, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *convrot_status_string(int status);
 

@@ -92,6 +92,8 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
         "convrot_int8_linear_shared_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc),
                                                  i32, i32, ctypes.POINTER(LinearDesc), vp, sz, vp]),
         "convrot_int8_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
+        "int4_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
+        "convrot_int4_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "convrot_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sigs.items():
@@ -221,6 +223,36 @@ def int8_linear(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, Y=No
                                _stream(stream, Y))
     _check("int8_linear", rc)
     return Y
+
+
+def int4_linear(Qx, s_x, W4, s_w=None, bias=None, input_scale: float = 1.0, Y=None,
+                y_dtype: int = F32, M: int | None = None, stream=None):
+    """int8_linear with convrot_w4a4 weights W4 (uint8 [N, K/2], two signed
+    4-bit values per byte, low nibble first)."""
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = W4.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=W4.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    rc = library().int4_linear(_ptr(Qx), _ptr(s_x), M, K, _ptr(W4), _ptr(s_w), _ptr(bias), N,
+                               ctypes.c_float(input_scale), _ptr(Y), _dtype_code(Y), ldy,
+                               _stream(stream, Y))
+    _check("int4_linear", rc)
+    return Y
+
+
+def convrot_int4_gemm_i32(Qx, W4, A=None, M: int | None = None, stream=None):
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = W4.shape[0]
+    if A is None:
+        A = torch.empty((M, N), dtype=torch.int32, device=W4.device)
+    rc = library().convrot_int4_gemm_i32(_ptr(Qx), _ptr(W4), M, K, N, _ptr(A), _stream(stream, A))
+    _check("convrot_int4_gemm_i32", rc)
+    return A
 
 
 def convrot_int8_gemm_i32(Qx, Qw, A=None, M: int | None = None, stream=None):

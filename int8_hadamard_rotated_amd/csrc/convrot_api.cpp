@@ -15,6 +15,7 @@ using namespace convrot_detail;
 namespace {
 
 constexpr int64_t kMaxContractionK = 133120;   // largest multiple of 64 with K * 127^2 < 2^31
+constexpr int64_t kMaxContractionK4 = 132096;  // largest multiple of 64 with 16 * K * 127 * 8 < 2^31
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -91,7 +92,7 @@ struct LinearCheck {
 
 int check_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t M, int64_t K,
                  int64_t N, float alpha, const void *Y, int y_dtype, int64_t ldy, bool need_scales,
-                 LinearCheck *out)
+                 LinearCheck *out, int w_bits = 8)
 {
     if (N < 0 || ldy < N)
         return CONVROT_EINVAL;
@@ -108,7 +109,7 @@ int check_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t 
         if (!aligned(Y, (uintptr_t)ye))
             return CONVROT_EINVAL;
         out->y = rows_span(Y, M, N, ldy, ye);
-        out->qw = span_of(Qw, N * K);
+        out->qw = span_of(Qw, w_bits == 4 ? N * (K / 2) : N * K);
         out->sw = need_scales ? span_of(s_w, 4 * N) : Span{};
         out->b = need_scales ? span_of(bias, 4 * N) : Span{};
     }
@@ -120,13 +121,13 @@ bool y_hits_weights(const LinearCheck &c, const LinearCheck &w)
     return overlap(c.y, w.qw) || overlap(c.y, w.sw) || overlap(c.y, w.b);
 }
 
-int check_contraction_k(int64_t K)
+int check_contraction_k(int64_t K, int w_bits = 8)
 {
     if (K < 1)
         return CONVROT_EINVAL;
     if (K % 64 != 0)
         return CONVROT_EUNSUPPORTED;
-    if (K > kMaxContractionK)
+    if (K > (w_bits == 4 ? kMaxContractionK4 : kMaxContractionK))
         return CONVROT_EOVERFLOW;
     return CONVROT_OK;
 }
@@ -222,17 +223,21 @@ int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int6
                                      packed, stream);
 }
 
-int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+}  // extern "C"
+
+namespace {
+
+int linear_impl(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
                 const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
-                int y_dtype, int64_t ldy, void *stream)
+                int y_dtype, int64_t ldy, void *stream, int w_bits)
 {
     if (M < 0)
         return CONVROT_EINVAL;
-    int rc = check_contraction_k(K);
+    int rc = check_contraction_k(K, w_bits);
     if (rc != CONVROT_OK)
         return rc;
     LinearCheck c;
-    rc = check_linear(Qw, s_w, bias, M, K, N, input_scale, Y, y_dtype, ldy, true, &c);
+    rc = check_linear(Qw, s_w, bias, M, K, N, input_scale, Y, y_dtype, ldy, true, &c, w_bits);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0 || N == 0)
@@ -248,22 +253,23 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
     p.s_x = s_x;
     p.M = M;
     p.K = K;
+    p.w_bits = w_bits;
     p.n_lin = 1;
     p.lin[0] = make_linear(Qw, s_w, bias, N, input_scale, Y, out_kind_of(y_dtype), ldy);
     (void)hipGetLastError();
     return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
-int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
-                          int32_t *A, void *stream)
+int gemm_i32_impl(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
+                  int32_t *A, void *stream, int w_bits)
 {
     if (M < 0)
         return CONVROT_EINVAL;
-    int rc = check_contraction_k(K);
+    int rc = check_contraction_k(K, w_bits);
     if (rc != CONVROT_OK)
         return rc;
     LinearCheck c;
-    rc = check_linear(Qw, nullptr, nullptr, M, K, N, 1.0f, A, CONVROT_F32, N, false, &c);
+    rc = check_linear(Qw, nullptr, nullptr, M, K, N, 1.0f, A, CONVROT_F32, N, false, &c, w_bits);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0 || N == 0)
@@ -278,10 +284,42 @@ int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t
     p.s_x = nullptr;
     p.M = M;
     p.K = K;
+    p.w_bits = w_bits;
     p.n_lin = 1;
     p.lin[0] = make_linear(Qw, nullptr, nullptr, N, 1.0f, A, kOutI32, N);
     (void)hipGetLastError();
     return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+                const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
+                int y_dtype, int64_t ldy, void *stream)
+{
+    return linear_impl(Qx, s_x, M, K, Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy, stream, 8);
+}
+
+int int4_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const uint8_t *W4,
+                const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
+                int y_dtype, int64_t ldy, void *stream)
+{
+    return linear_impl(Qx, s_x, M, K, reinterpret_cast<const int8_t *>(W4), s_w, bias, N,
+                       input_scale, Y, y_dtype, ldy, stream, 4);
+}
+
+int convrot_int4_gemm_i32(const int8_t *Qx, const uint8_t *W4, int64_t M, int64_t K, int64_t N,
+                          int32_t *A, void *stream)
+{
+    return gemm_i32_impl(Qx, reinterpret_cast<const int8_t *>(W4), M, K, N, A, stream, 4);
+}
+
+int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
+                          int32_t *A, void *stream)
+{
+    return gemm_i32_impl(Qx, Qw, M, K, N, A, stream, 8);
 }
 
 int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -362,6 +400,7 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
         p.s_x = reinterpret_cast<const float *>(base + s * slot_bytes + m_pad * K);
         p.M = M;
         p.K = K;
+        p.w_bits = 8;
         for (int i = 0; i < n; ++i) {
             if (slot_of[i] != s || descs[i].N == 0)
                 continue;

@@ -43,7 +43,7 @@ constexpr int kGroupM = 4;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kBK = 64;                    // K bytes per step (one MFMA K)
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int WB>
 struct Tile {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
@@ -51,13 +51,19 @@ struct Tile {
     static constexpr int kWaveN = BN / WN;
     static constexpr int kTM = kWaveM / 16;                // A blocks per wave
     static constexpr int kTN = kWaveN / 16;                // B blocks per wave
-    static constexpr int kStride = kBK;                    // LDS bytes per row (swizzled)
-    static constexpr int kStageBytes = (BM + BN) * kStride;
+    static constexpr int kStride = kBK;                    // LDS bytes per A row (swizzled)
+    static constexpr int kStrideB = WB == 4 ? kBK / 2 : kBK;   // LDS bytes per B row (packed when 4-bit)
+    static constexpr int kABytes = BM * kStride;
+    static constexpr int kStageBytes = kABytes + BN * kStrideB;
     static constexpr int kStages = STAGES;                 // LDS ring depth
-    static constexpr int kLoads = (BM + BN) / (16 * kWaves);   // DMA loads per wave per step
+    static constexpr int kRowsPerDmaB = 1024 / kStrideB;   // B rows per 1 KB DMA instruction
+    static constexpr int kDmaA = BM / 16, kDmaB = BN / kRowsPerDmaB;
+    static constexpr int kDma = kDmaA + kDmaB;             // DMA instructions per step
+    static constexpr int kLoads = (kDma + kWaves - 1) / kWaves;   // at most, per wave per step
     static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w [BN], bias [BN]
     static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 2 * BN);
-    static_assert((BM + BN) % (16 * kWaves) == 0, "whole 16-row DMA blocks per wave");
+    static_assert(WB == 8 || WB == 4, "weight bits");
+    static_assert(BN % kRowsPerDmaB == 0, "whole B DMA blocks");
     static_assert(BM % 16 == 0 && kWaveM % 16 == 0 && kWaveN % 16 == 0, "");
     static_assert(kLoads <= kTM, "at most one DMA load per MFMA group");
     static_assert(STAGES >= 4, "ring depth");
@@ -107,9 +113,9 @@ __device__ __forceinline__ void wait_vmcnt()
 // low-bit-XOR layouts, which cost two LDS passes per read.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
-// Wait until at most n of this wave's DMA loads are outstanding (n a
-// multiple of LOADS, at most MAXN).
-template <int LOADS, int MAXN>
+// Wait until at most n of this wave's DMA loads are outstanding (0 <= n,
+// values above MAXN wait for MAXN).
+template <int MAXN>
 __device__ __forceinline__ void wait_vmcnt_le(int n)
 {
     if constexpr (MAXN <= 0) {
@@ -118,15 +124,29 @@ __device__ __forceinline__ void wait_vmcnt_le(int n)
         if (n >= MAXN)
             wait_vmcnt<MAXN>();
         else
-            wait_vmcnt_le<LOADS, MAXN - LOADS>(n);
+            wait_vmcnt_le<MAXN - 1>(n);
     }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool DIV>
+// Packed 4-bit weights: 8 bytes (16 two's-complement nibbles, the even
+// feature in the low nibble) -> 16 int8 lanes of an MFMA operand, each holding
+// 16 times its weight (the nibble moved to the top of its byte, which is the
+// same two's-complement value scaled by 16).  The contraction then yields
+// exactly 16 A; the epilogue shifts it back.
+__device__ __forceinline__ v4i expand_w4(v2u p)
+{
+    const unsigned lo0 = (p.x << 4) & 0xF0F0F0F0u, hi0 = p.x & 0xF0F0F0F0u;
+    const unsigned lo1 = (p.y << 4) & 0xF0F0F0F0u, hi1 = p.y & 0xF0F0F0F0u;
+    // byte i of the result: element i; from {hi, lo} pick lo.b0 hi.b0 lo.b1 hi.b1 / lo.b2 hi.b2 lo.b3 hi.b3
+    return v4i{(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u), (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
+               (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u), (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool DIV, int WB>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     GemmProblem p, int tiles_m, int total_tiles)
 {
-    using T = Tile<BM, BN, WM, WN, STAGES>;
+    using T = Tile<BM, BN, WM, WN, STAGES, WB>;
     __shared__ __attribute__((aligned(16))) int8_t lds[T::kLdsBytes];
 
     // ---- tile assignment: contiguous tile range per XCD, then group-M order
@@ -153,32 +173,42 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- global -> LDS by direct buffer loads.  A stage holds the BM rows
-    // of the A tile followed by the BN rows of the B tile, 64 bytes each; the
-    // DMA instruction g of a step moves rows 16 g .. 16 g + 15 of that list
-    // (1 KB): lane L writes row 16 g + L/4, slot L%4, which receives logical
-    // K chunk (L%4) ^ swz(row).  swz only depends on row bits 1..2, that is on
-    // L/4, so one per-lane offset serves every instruction.  Wave w issues
-    // instructions g = kWaves * q + w, q < kLoads.
+    // of the A tile (64 bytes each) followed by the BN rows of the B tile
+    // (64 bytes each, or 32 for packed 4-bit weights).  A DMA instruction moves
+    // 1 KB: A instruction g moves rows 16 g .. 16 g + 15 (lane L writes row
+    // 16 g + L/4, slot L%4, which receives logical K chunk (L%4) ^ swz(row));
+    // a 4-bit B instruction moves 32 rows of 32 bytes (lane L writes row L/2,
+    // half L%2, which receives logical half (L%2) ^ (row bit 3)).  The
+    // swizzles only depend on row bits below the block size, so one per-lane
+    // offset serves every instruction.  Wave w issues instructions
+    // g = kWaves * q + w (g < kDma), one per MFMA group.
     //
     // Each operand tile is addressed through a buffer descriptor that starts
     // at the tile's first row and ends after its last valid row; rows past M
     // (or N) fall outside it and are never stored.
+    const int64_t kb = WB == 4 ? K / 2 : K;                   // weight bytes per row
     const int64_t a_rows = (M - m0) < BM ? (M - m0) : BM;
     const int64_t b_rows = (N - n0) < BN ? (N - n0) : BN;
     const v4u a_rsrc = buffer_rsrc(p.Qx + m0 * K, (uint32_t)(a_rows * K));
-    const v4u b_rsrc = buffer_rsrc(L.Qw + n0 * K, (uint32_t)(b_rows * K));
+    const v4u b_rsrc = buffer_rsrc(L.Qw + n0 * kb, (uint32_t)(b_rows * kb));
     const int ld_row = lane >> 2;
     const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
+    const int ld_voff_b = WB == 4 ? (lane >> 1) * (int)kb + 16 * ((lane & 1) ^ ((lane >> 4) & 1))
+                                  : ld_voff;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t *)lds;
+    // DMA instructions this wave issues per step
+    const int my_loads = (T::kDma - wave + T::kWaves - 1) / T::kWaves;
 
     auto issue_one = [&](int step, int q) {
         const uint32_t st = lds_base + (uint32_t)(step % T::kStages) * T::kStageBytes;
-        const int k0 = step * kBK;
         const int g = T::kWaves * q + wave;
-        if (16 * g < BM)
-            dma_x4(a_rsrc, ld_voff, 16 * g * (int)K + k0, st + 16 * g * T::kStride);
-        else
-            dma_x4(b_rsrc, ld_voff, (16 * g - BM) * (int)K + k0, st + 16 * g * T::kStride);
+        if (g < T::kDmaA) {
+            dma_x4(a_rsrc, ld_voff, 16 * g * (int)K + step * kBK, st + 1024 * g);
+        } else if (g < T::kDma) {
+            const int gb = g - T::kDmaA;
+            dma_x4(b_rsrc, ld_voff_b, T::kRowsPerDmaB * gb * (int)kb + step * T::kStrideB,
+                   st + T::kABytes + 1024 * gb);
+        }
     };
 
     // The epilogue's row scales, weight scales and bias go to LDS first, by
@@ -224,14 +254,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int frag_row = lane & 15, frag_chunk = lane >> 4;
     const int frag_slot = 16 * (frag_chunk ^ swz(frag_row));
     const int a_frag0 = (wm * T::kWaveM + frag_row) * T::kStride + frag_slot;
-    const int b_frag0 = (BM + wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
+    // 4-bit B rows: lane l reads the 8 packed bytes of logical K chunk l/16,
+    // stored at 8-byte slot (l/16) ^ (2 * row bit 3) of its 32-byte row
+    const int b_frag0 = WB == 4 ? T::kABytes + (wn * T::kWaveN + frag_row) * T::kStrideB +
+                                      8 * (frag_chunk ^ (2 * ((frag_row >> 3) & 1)))
+                                : T::kABytes + (wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
     auto read_a = [&](int stage, int i) {
         return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + a_frag0 +
                                               i * 16 * T::kStride);
     };
     auto read_b = [&](int stage, int j) {
-        return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + b_frag0 +
-                                              j * 16 * T::kStride);
+        if constexpr (WB == 4)
+            return expand_w4(*reinterpret_cast<const v2u *>(lds + stage * T::kStageBytes + b_frag0 +
+                                                            j * 16 * T::kStrideB));
+        else
+            return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + b_frag0 +
+                                                  j * 16 * T::kStride);
     };
 
     // ---- main loop, software-pipelined one K-step ahead on fragments.
@@ -255,7 +293,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         if (has_next) {
             // step k+1 must have landed; steps k+2 .. k+S-2 may stay in flight
             const int younger = (ksteps - k - 2) < (S - 3) ? (ksteps - k - 2) : (S - 3);
-            wait_vmcnt_le<T::kLoads, (S - 3) * T::kLoads>(younger * T::kLoads);
+            wait_vmcnt_le<(S - 3) * T::kLoads>(younger * my_loads);
             __syncthreads();
         }
         const int next_stage = (k + 1) % S;
@@ -287,7 +325,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     {
         // step 0 must have landed (and the older scale loads)
         const int younger = (ksteps - 1) < (S - 2) ? (ksteps - 1) : (S - 2);
-        wait_vmcnt_le<T::kLoads, (S - 2) * T::kLoads>(younger * T::kLoads);
+        wait_vmcnt_le<(S - 2) * T::kLoads>(younger * my_loads);
     }
     __syncthreads();
 #pragma unroll
@@ -340,7 +378,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
+                stage[(row_in + v) * kStageStride + j * 16 + col_in] =
+                    WB == 4 ? (acc[i][j][v] >> 4) : acc[i][j][v];   // 4-bit weights: 16 A
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             const int rr = rr0 + kRowStep * sl;
@@ -401,10 +440,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int WB>
 hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
 {
-    using T = Tile<BM, BN, WM, WN, STAGES>;
+    using T = Tile<BM, BN, WM, WN, STAGES, WB>;
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     int total = 0;
     for (int d = 0; d < p.n_lin; ++d) {
@@ -419,10 +458,10 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     for (int d = 0; d < p.n_lin; ++d)
         div = div || p.lin[d].alpha != 1.0f;
     if (div)
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, true>), dim3(total), dim3(T::kThreads),
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, true, WB>), dim3(total), dim3(T::kThreads),
                            0, stream, p, tiles_m, total);
     else
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, false>), dim3(total), dim3(T::kThreads),
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, false, WB>), dim3(total), dim3(T::kThreads),
                            0, stream, p, tiles_m, total);
     return hipGetLastError();
 }
@@ -441,9 +480,14 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
     int64_t big = 0;
     for (int d = 0; d < p.n_lin; ++d)
         big += ((p.M + 255) / 256) * ((p.lin[d].N + 255) / 256);
+    if (p.w_bits == 4) {
+        if (big >= 256)
+            return launch_tiled<256, 256, 4, 4, 4, 4>(p, stream);
+        return launch_tiled<128, 128, 2, 4, 4, 4>(p, stream);
+    }
     if (big >= 256)
-        return launch_tiled<256, 256, 4, 4, 4>(p, stream);
-    return launch_tiled<128, 128, 2, 4, 4>(p, stream);
+        return launch_tiled<256, 256, 4, 4, 4, 8>(p, stream);
+    return launch_tiled<128, 128, 2, 4, 4, 8>(p, stream);
 }
 
 }  // namespace convrot_detail

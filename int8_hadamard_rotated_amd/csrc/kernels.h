@@ -50,6 +50,7 @@ struct GemmProblem {
     const float *s_x;    // [M]
     int64_t M;
     int64_t K;
+    int w_bits;          // 8: Qw int8 [N][K]; 4: Qw packed 4-bit [N][K/2] (low nibble first)
     int n_lin;
     GemmLinear lin[kMaxLinears];
 };

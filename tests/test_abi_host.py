@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     assert header_functions() == sorted([
         "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
-        "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre"])
+        "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
+        "int4_linear", "convrot_int4_gemm_i32"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -153,6 +154,24 @@ def test_int8_linear_validation(lib):
     assert lin(lib, N=0) == OK
     # the largest K that is still exact passes the K check (then fails on Qx)
     assert lin(lib, K=133120, Qx=0) == EINVAL
+
+
+def test_int4_linear_validation(lib):
+    def l4(K=256, W4=BASE + 16 * MB, Y=BASE + 32 * MB, M=8, N=32):
+        return lib.int4_linear(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + 8 * MB), M, K,
+                               ctypes.c_void_p(W4), None, None, N, ctypes.c_float(1.0),
+                               ctypes.c_void_p(Y), cr.F32, N, None)
+    assert l4(K=132160) == EOVF                          # 16 * K * 127 * 8 would exceed int32
+    assert l4(K=132096, W4=0) == EINVAL                  # the largest exact K passes the K check
+    assert l4(K=96) == EUNSUP
+    assert l4(W4=BASE + 16 * MB + 8) == EINVAL           # 16-byte aligned weights
+    # Y overlapping the packed weights (N * K/2 bytes), not beyond them
+    assert l4(Y=BASE + 16 * MB + 32 * 128 - 64) == EOVL
+    assert l4(M=0) == OK
+    f = lib.convrot_int4_gemm_i32
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), 4, 132160, 4,
+             ctypes.c_void_p(BASE + 2 * MB), None) == EOVF
+    assert f(None, None, 0, 64, 4, None, None) == OK
 
 
 def test_gemm_i32_validation(lib):

@@ -21,6 +21,10 @@ Recipe, per workload (fixed draw order):
     for each linear j:
         W_j = rng.standard_normal((N, K), float32) * 0.02
         b_j = rng.standard_normal(N, float32) * 0.1
+    for 4-bit weights (convrot_w4a4) instead, per linear j:
+        W4_j = rng.integers(0, 256, (N, K/2), uint8)            # every nibble value
+        s_w_j = exp(rng.uniform(log 1e-3, log 1e-2, N)) as float32
+        b_j = rng.standard_normal(N, float32) * 0.1
     when the workload has a Modulate producer (per-channel vectors, as the
     adaLN modulation of a DiT block supplies them):
         scale = rng.standard_normal(K, float32) * 0.3
@@ -50,6 +54,7 @@ class Workload:
     outlier_p: float = 0.005
     outlier_f: float = 30.0
     modulate: bool = False            # a Modulate producer before the rotation
+    w_bits: int = 8                   # 4: convrot_w4a4 packed weights
     note: str = ""
 
     @property
@@ -70,6 +75,8 @@ WORKLOADS = {
     "mlp_up_mod": Workload("mlp_up_mod", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=5,
                            modulate=True,
                            note="DiT MLP up-projection with its Modulate producer fused"),
+    "mlp_up_w4": Workload("mlp_up_w4", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=6,
+                          w_bits=4, note="DiT MLP up-projection with convrot_w4a4 weights"),
     "mlp_down": Workload("mlp_down", 16384, 12288, 3072, 256, BF16, BF16, (1.0,), seed=4,
                          note="batched MLP down-projection, 4 images x 4096 tokens, bf16 in/out"),
 }
@@ -117,6 +124,7 @@ class Inputs:
     X: np.ndarray                      # float32 or uint16 (bf16 bits), [M,K]
     W: list = field(default_factory=list)   # float32 [N,K] per linear
     b: list = field(default_factory=list)   # float32 [N] per linear
+    s_w: list = field(default_factory=list) # float32 [N] per linear (4-bit weights only)
     mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
     mod_shift: np.ndarray | None = None     # float32 [K]
 
@@ -131,6 +139,11 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
     X = gaussian_activations(rng, rows, w.K, w.outlier_p, w.outlier_f, w.x_dtype)
     inp = Inputs(w, X)
     for _ in range(w.n_linears):
+        if w.w_bits == 4:
+            inp.W.append(random_int4_packed(rng, w.N, w.K))
+            inp.s_w.append(random_scales(rng, w.N, 1e-3, 1e-2))
+            inp.b.append(rng.standard_normal(w.N, dtype=np.float32) * np.float32(0.1))
+            continue
         W, b = gaussian_weights(rng, w.N, w.K)
         inp.W.append(W)
         inp.b.append(b)
@@ -144,6 +157,11 @@ def modulation(rng: np.random.Generator, K: int, sigma: float = 0.3):
     sc = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
     sh = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
     return sc, sh
+
+
+def random_int4_packed(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """Uniform bytes [N, K/2]: packed 4-bit weights covering every nibble value."""
+    return rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
 
 
 def random_codes(rng: np.random.Generator, shape, lo: int = -127, hi: int = 127) -> np.ndarray:
