@@ -98,6 +98,7 @@ class Oracle:
             "oracle_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i32]),
             "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
             "oracle_unpack_int4": (i32, [vp, i64, i64, vp]),
+            "oracle_gated_residual": (i32, [vp, i64, i64, f32, vp, vp, i32, i64, i32, vp, i64, i32]),
             "oracle_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, i32]),
             "oracle_epilogue": (i32, [vp, i64, i64, vp, vp, vp, f32, i32, vp, i64, i32]),
             "oracle_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
@@ -198,6 +199,22 @@ class Oracle:
                                       y_dtype, _p(Y), N, threads)
         self._check(rc, "epilogue")
         return Y
+
+    def gated_residual(self, Y: np.ndarray, gate: np.ndarray, R: np.ndarray, scale: float = 1.0,
+                       z_dtype: int = F32, threads: int = 1) -> np.ndarray:
+        """The gated-residual epilogue on a binary32 reconstruction Y [M, N]:
+        residual R [M, N] (float32 or bf16 bits), per-channel gate [N]."""
+        Y = np.ascontiguousarray(Y, dtype=np.float32)
+        M, N = Y.shape
+        g = np.ascontiguousarray(gate, dtype=np.float32)
+        code = _dtype_code(R)
+        R = np.ascontiguousarray(R)
+        assert g.shape == (N,) and R.shape == (M, N)
+        Z = np.empty((M, N), dtype=np.float32 if z_dtype == F32 else np.uint16)
+        rc = self.lib.oracle_gated_residual(_p(Y), M, N, ctypes.c_float(scale), _p(g), _p(R), code, N,
+                                            z_dtype, _p(Z), N, threads)
+        self._check(rc, "gated_residual")
+        return Z
 
     def linear(self, X: np.ndarray, G: int, Qw: np.ndarray, s_w, bias, alpha: float = 1.0,
                y_dtype: int = F32, threads: int = 1) -> np.ndarray:

@@ -35,6 +35,12 @@
  *     byte, the low nibble holding the even input feature; they are decoded
  *     to int8 and then take the same contraction and reconstruction as INT8
  *     weights (the activations use the INT8 convrot quantization unchanged).
+ *   - the gated-residual epilogue (page "ggml operator extensions", section
+ *     "sd.cpp integration": INT8 GEMM -> [Scale] -> Mul(gate) -> Add(residual))
+ *     continues from the binary32 reconstruction: an optional scalar scale,
+ *     then a per-channel gate vector of length N shared by every row, then a
+ *     residual of the output's shape and dtype, each a separately rounded
+ *     binary32 operation; the result takes the output cast.
  *   - the Modulate producer (page "ggml operator extensions", section
  *     "sd.cpp integration", the Modulate operator and its ConvRot fusion) is
  *     applied to the widened binary32 input with per-channel vectors of
@@ -376,6 +382,41 @@ int oracle_epilogue(const int32_t *A, int64_t M, int64_t N, const float *s_x, co
 }
 
 /* ----------------------------------------------------------- whole linear */
+
+/* --------------------------------------------------------- gated residual */
+
+/*
+ * Z[r, o] = cast(fl(fl(fl(Y[r, o] * scale) * gate[o]) + widen(R[r, o])))
+ * (page "ggml operator extensions", section "sd.cpp integration", the INT8
+ * gated-residual fusion; the scale multiply only when scale != 1).  Y is the
+ * binary32 reconstruction [M][N] (row stride N), R the residual [M][ldr] in
+ * r_dtype, Z [M][ldz] in z_dtype (bf16 by round to nearest even).
+ */
+int oracle_gated_residual(const float *Y, int64_t M, int64_t N, float scale, const float *gate,
+                          const void *R, int r_dtype, int64_t ldr, int z_dtype, void *Z,
+                          int64_t ldz, int threads)
+{
+    if (!Y || !gate || !R || !Z || M < 0 || N < 0 || ldr < N || ldz < N)
+        return ORACLE_EINVAL;
+    if ((r_dtype != ORACLE_F32 && r_dtype != ORACLE_BF16) ||
+        (z_dtype != ORACLE_F32 && z_dtype != ORACLE_BF16))
+        return ORACLE_EUNSUPPORTED;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t r = 0; r < M; ++r) {
+        for (int64_t o = 0; o < N; ++o) {
+            float t = Y[r * N + o];
+            if (scale != 1.0f)
+                t = t * scale;
+            t = t * gate[o];
+            t = t + load_widened(R, r_dtype, r * ldr + o);
+            if (z_dtype == ORACLE_F32)
+                ((float *)Z)[r * ldz + o] = t;
+            else
+                ((uint16_t *)Z)[r * ldz + o] = f32_to_bf16_rne(t);
+        }
+    }
+    return ORACLE_OK;
+}
 
 /*
  * The complete layer for one linear: quantize (packed), contract, reconstruct.

@@ -462,4 +462,43 @@ def pin_int4_roundtrip(o):
             assert int(A[r, n]) == sum(int(Qx[r, k]) * int(Q[n, k]) for k in range(256))
 
 
+def pin_gated_residual_exact(o):
+    """The gated-residual epilogue against exact rational arithmetic with
+    binary32 rounding at each step: fl(fl(fl(y * scale) * gate) + r), scale
+    only when != 1, gate indexed by column; residual and output in binary32
+    and bf16 (page "ggml operator extensions", INT8 gated residual)."""
+    rng = np.random.default_rng(44)
+    M, N = 3, 40
+    Y = (rng.standard_normal((M, N)) * 3.0).astype(np.float32)
+    g = (rng.standard_normal(N) * 0.7).astype(np.float32)
+    Rf = rng.standard_normal((M, N)).astype(np.float32)
+    Rb = workloads.f32_to_bf16_bits(Rf)
+    for R, rw in ((Rf, Rf), (Rb, workloads.bf16_bits_to_f32(Rb))):
+        for scale in (1.0, 0.37):
+            for zd in (oracle_pkg.F32, oracle_pkg.BF16):
+                Z = o.gated_residual(Y, g, R, scale, zd)
+                for r in range(M):
+                    for i in range(N):
+                        t = F(Y[r, i])
+                        if scale != 1.0:
+                            t = rne_f32(t * F(np.float32(scale)))
+                        t = rne_f32(rne_f32(t * F(g[i])) + F(rw[r, i]))
+                        if zd == oracle_pkg.F32:
+                            assert F(Z[r, i]) == t, f"gated residual ({r},{i})"
+                        else:   # the bf16 cast itself is pinned by pin_bf16_output
+                            tb = workloads.f32_to_bf16_bits(np.array([float(t)], np.float32))[0]
+                            assert int(Z[r, i]) == int(tb), f"gated residual bf16 ({r},{i})"
+
+
+def pin_gated_residual_special_cases(o):
+    """gate = 0 leaves exactly the residual; gate = 1 with a zero residual and
+    no scale leaves exactly the reconstruction."""
+    rng = np.random.default_rng(45)
+    M, N = 5, 64
+    Y = (rng.standard_normal((M, N)) * 3.0).astype(np.float32)
+    R = (rng.standard_normal((M, N)) + 0.5).astype(np.float32)
+    assert np.array_equal(o.gated_residual(Y, np.zeros(N, np.float32), R), R)
+    assert np.array_equal(o.gated_residual(Y, np.ones(N, np.float32), np.zeros((M, N), np.float32)), Y)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,11 @@ MUTATIONS = {
                                "const int nib = (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
     "int4_offset_binary": ("Qw[o * K + k] = (int8_t)(nib >= 8 ? nib - 16 : nib);",
                            "Qw[o * K + k] = (int8_t)(nib - 8);"),
+    "residual_before_gate": ("            t = t * gate[o];\n            t = t + load_widened(R, r_dtype, r * ldr + o);",
+                             "            t = t + load_widened(R, r_dtype, r * ldr + o);\n            t = t * gate[o];"),
+    "gate_scale_fused": ("            if (scale != 1.0f)\n                t = t * scale;\n            t = t * gate[o];",
+                         "            t = t * (scale * gate[o]);"),
+    "gate_row_index": ("t = t * gate[o];", "t = t * gate[r % N];"),
     "zero_row_scale": ("        *s_out = 0.0f;\n        memset(q, 0, (size_t)K);\n        return;",
                        "        m = 1.0f;"),
 }
