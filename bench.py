@@ -157,12 +157,17 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     t0 = time.perf_counter()
     if w.modulate:
         X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
-    o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
+    if w.gated:
+        Yf = o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], oracle.F32, threads=threads)
+        o.gated_residual(Yf, inp.gate, np.ascontiguousarray(inp.residual[:rows]), 1.0, yd,
+                         threads=threads)
+    else:
+        o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
     dt = time.perf_counter() - t0
     ops = 2 * rows * w.N * w.K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {w.M} rows of {w.name} ({'modulate + ' if w.modulate else ''}"
-                      f"quantize + int32 GEMM + reconstruction "
+                      f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''} "
                       f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
 
 
@@ -235,6 +240,8 @@ def main() -> int:
                          device=dev)
         Ys = [torch.empty((w.M, w.N), dtype=torch.bfloat16 if yd == cr.BF16 else torch.float32,
                           device=dev) for _ in range(w.n_linears)]
+        if w.gated:                  # the output starts as the residual (updated in place)
+            Ys[0].copy_(to_dev_x(inp.residual, torch))
         sets.append((Xd, ws, Ys))
 
     mod = (cr.Modulate(torch.from_numpy(inp.mod_scale).to(dev), torch.from_numpy(inp.mod_shift).to(dev))
@@ -247,10 +254,16 @@ def main() -> int:
         else:
             cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
 
+    gate = torch.from_numpy(inp.gate).to(dev) if w.gated else None
+
     def gemm(i):
         Xd, ws, Ys = sets[i % n_sets]
         l = lins[0]
         qx, sx = views[i % n_sets]
+        if w.gated:
+            cr.int8_linear_post(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"],
+                                cr.GatedResidual(gate, Ys[0]), Y=Ys[0], M=w.M)
+            return
         lin_fn = cr.int4_linear if w.w_bits == 4 else cr.int8_linear
         lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
 
@@ -311,7 +324,8 @@ def main() -> int:
         "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W {'i4' if w.w_bits == 4 else 'i8'} [{w.N},{w.K}] x "
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
                                f"{list(w.input_scales)}"
-                               + (", Modulate producer fused" if w.modulate else ""),
+                               + (", Modulate producer fused" if w.modulate else "")
+                               + (", gated residual in place" if w.gated else ""),
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,
                    "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets},
         "step_us_events": round(ev_step_us, 3),

@@ -189,6 +189,38 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
 int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
                           int32_t *A, void *stream);
 
+/* An epilogue applied after the reconstruction, before the output cast.
+ *
+ * CONVROT_POST_GATED_RESIDUAL (page "ggml operator extensions", section
+ * "sd.cpp integration": INT8 GEMM -> [Scale] -> Mul(gate) -> Add(residual),
+ * separate FP32 rounding of the gate multiplication and the residual
+ * addition):
+ *     y' = fl(fl(fl(y * scale) * gate[o]) + residual[r][o])
+ * where the scale multiply happens only when scale != 1, gate is a device
+ * vector of N floats shared by every row (4-byte aligned) and residual is a
+ * device [M][ld_residual] tensor in the output dtype (bf16 widened exactly).
+ * The residual may be Y itself (same base and row stride: an exact in-place
+ * residual); any other overlap with Y, or a gate overlapping Y, is
+ * CONVROT_EOVERLAP. */
+typedef enum { CONVROT_POST_NONE = 0, CONVROT_POST_GATED_RESIDUAL = 1 } convrot_post_kind;
+
+typedef struct {
+    int kind;               /* convrot_post_kind */
+    float scale;            /* GATED_RESIDUAL: scalar multiply first (1 = none) */
+    const float *gate;      /* GATED_RESIDUAL: [N] (device) */
+    const void *residual;   /* GATED_RESIDUAL: [M][ld_residual] (device), output dtype */
+    int64_t ld_residual;    /* elements, >= N */
+} convrot_post;
+
+/* int8_linear followed by an epilogue (post may be NULL or of kind
+ * CONVROT_POST_NONE: then identical to int8_linear).  CONVROT_EINVAL for a
+ * GATED_RESIDUAL descriptor with a missing or misaligned gate or residual, a
+ * row stride below N or a non-finite scale; CONVROT_EUNSUPPORTED for an
+ * unknown kind. */
+int int8_linear_post(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+                     const float *s_w, const float *bias, int64_t N, float input_scale,
+                     const convrot_post *post, void *Y, int y_dtype, int64_t ldy, void *stream);
+
 /* 4-bit weights, format convrot_w4a4 (page "INT8 Convrot Safetensors",
  * section "Packed INT4 convrot"): W4 is [N][K/2] bytes, feature k of output o
  * in byte o*K/2 + k/2, low nibble for even k, high nibble for odd k, each a

@@ -17,6 +17,7 @@ LIBRARY = os.path.join(_HERE, "libconvrot.so")
 OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 PRE_NONE, PRE_MODULATE = 0, 1
+POST_NONE, POST_GATED_RESIDUAL = 0, 1
 MAX_LINEARS = 16
 
 _lib = None
@@ -64,6 +65,33 @@ class Modulate:
                        None if self.shift is None else self.shift.data_ptr())
 
 
+class PostDesc(ctypes.Structure):
+    """Mirror of convrot_post."""
+    _fields_ = [
+        ("kind", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("gate", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+        ("ld_residual", ctypes.c_int64),
+    ]
+
+
+class GatedResidual:
+    """The gated-residual epilogue: fl(fl(fl(y * scale) * gate) + residual);
+    gate float32 [N], residual [M, N] (row-contiguous last dimension) in the
+    output dtype; the residual may be the output tensor itself."""
+
+    def __init__(self, gate, residual, scale: float = 1.0):
+        self.gate = gate
+        self.residual = residual
+        self.scale = scale
+
+    def desc(self) -> PostDesc:
+        ld = _row_stride(self.residual) if self.residual.shape[0] > 0 else self.residual.shape[1]
+        return PostDesc(POST_GATED_RESIDUAL, self.scale, self.gate.data_ptr(),
+                        self.residual.data_ptr(), ld)
+
+
 def _pre(pre):
     return None if pre is None else ctypes.byref(pre.desc())
 
@@ -93,6 +121,8 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                                                  i32, i32, ctypes.POINTER(LinearDesc), vp, sz, vp]),
         "convrot_int8_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "int4_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
+        "int8_linear_post": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32,
+                                   ctypes.POINTER(PostDesc), vp, i32, i64, vp]),
         "convrot_int4_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "convrot_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -222,6 +252,24 @@ def int8_linear(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, Y=No
                                ctypes.c_float(input_scale), _ptr(Y), _dtype_code(Y), ldy,
                                _stream(stream, Y))
     _check("int8_linear", rc)
+    return Y
+
+
+def int8_linear_post(Qx, s_x, Qw, s_w=None, bias=None, input_scale: float = 1.0, post=None,
+                     Y=None, y_dtype: int = F32, M: int | None = None, stream=None):
+    """int8_linear followed by an epilogue (a GatedResidual, or None)."""
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = Qw.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=Qw.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    d = None if post is None else ctypes.byref(post.desc())
+    rc = library().int8_linear_post(_ptr(Qx), _ptr(s_x), M, K, _ptr(Qw), _ptr(s_w), _ptr(bias), N,
+                                    ctypes.c_float(input_scale), d, _ptr(Y), _dtype_code(Y), ldy,
+                                    _stream(stream, Y))
+    _check("int8_linear_post", rc)
     return Y
 
 

@@ -227,9 +227,39 @@ int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int6
 
 namespace {
 
+// Validates an epilogue descriptor (nullable) for an [M][N] output Y.
+int check_post(const convrot_post *post, int64_t M, int64_t N, const void *Y, int y_dtype,
+               int64_t ldy, const Span &y, GemmLinear *l)
+{
+    if (!post || post->kind == CONVROT_POST_NONE)
+        return CONVROT_OK;
+    if (post->kind != CONVROT_POST_GATED_RESIDUAL)
+        return CONVROT_EUNSUPPORTED;
+    if (!std::isfinite(post->scale))
+        return CONVROT_EINVAL;
+    if (M == 0 || N == 0)
+        return CONVROT_OK;
+    const int64_t e = elem_bytes(y_dtype);
+    if (!post->gate || !aligned(post->gate, 4) || !post->residual ||
+        !aligned(post->residual, (uintptr_t)e) || post->ld_residual < N)
+        return CONVROT_EINVAL;
+    const Span rs = rows_span(post->residual, M, N, post->ld_residual, e);
+    const bool in_place = post->residual == Y && post->ld_residual == ldy;
+    if ((!in_place && overlap(rs, y)) || overlap(span_of(post->gate, 4 * N), y))
+        return CONVROT_EOVERLAP;
+    l->post = 1;
+    l->post_scale = post->scale;
+    l->gate = post->gate;
+    l->residual = post->residual;
+    l->ld_res = post->ld_residual;
+    l->res_vec = (aligned(post->residual, y_dtype == CONVROT_BF16 ? 8 : 16) &&
+                  post->ld_residual % 4 == 0) ? 1 : 0;
+    return CONVROT_OK;
+}
+
 int linear_impl(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
                 const float *s_w, const float *bias, int64_t N, float input_scale, void *Y,
-                int y_dtype, int64_t ldy, void *stream, int w_bits)
+                int y_dtype, int64_t ldy, void *stream, int w_bits, const convrot_post *post = nullptr)
 {
     if (M < 0)
         return CONVROT_EINVAL;
@@ -238,6 +268,11 @@ int linear_impl(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
         return rc;
     LinearCheck c;
     rc = check_linear(Qw, s_w, bias, M, K, N, input_scale, Y, y_dtype, ldy, true, &c, w_bits);
+    if (rc != CONVROT_OK)
+        return rc;
+    GemmLinear post_fields;
+    std::memset(&post_fields, 0, sizeof post_fields);
+    rc = check_post(post, M, N, Y, y_dtype, ldy, c.y, &post_fields);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0 || N == 0)
@@ -256,6 +291,12 @@ int linear_impl(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
     p.w_bits = w_bits;
     p.n_lin = 1;
     p.lin[0] = make_linear(Qw, s_w, bias, N, input_scale, Y, out_kind_of(y_dtype), ldy);
+    p.lin[0].post = post_fields.post;
+    p.lin[0].post_scale = post_fields.post_scale;
+    p.lin[0].gate = post_fields.gate;
+    p.lin[0].residual = post_fields.residual;
+    p.lin[0].ld_res = post_fields.ld_res;
+    p.lin[0].res_vec = post_fields.res_vec;
     (void)hipGetLastError();
     return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
@@ -300,6 +341,14 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
                 int y_dtype, int64_t ldy, void *stream)
 {
     return linear_impl(Qx, s_x, M, K, Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy, stream, 8);
+}
+
+int int8_linear_post(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
+                     const float *s_w, const float *bias, int64_t N, float input_scale,
+                     const convrot_post *post, void *Y, int y_dtype, int64_t ldy, void *stream)
+{
+    return linear_impl(Qx, s_x, M, K, Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy, stream, 8,
+                       post);
 }
 
 int int4_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const uint8_t *W4,

@@ -60,14 +60,14 @@ struct Tile {
     static constexpr int kDmaA = BM / 16, kDmaB = BN / kRowsPerDmaB;
     static constexpr int kDma = kDmaA + kDmaB;             // DMA instructions per step
     static constexpr int kLoads = (kDma + kWaves - 1) / kWaves;   // at most, per wave per step
-    static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w [BN], bias [BN]
-    static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 2 * BN);
+    static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w, bias, gate [BN]
+    static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 3 * BN);
     static_assert(WB == 8 || WB == 4, "weight bits");
     static_assert(BN % kRowsPerDmaB == 0, "whole B DMA blocks");
     static_assert(BM % 16 == 0 && kWaveM % 16 == 0 && kWaveN % 16 == 0, "");
     static_assert(kLoads <= kTM, "at most one DMA load per MFMA group");
     static_assert(STAGES >= 4, "ring depth");
-    static_assert((BM + 2 * BN) % 64 == 0, "64-float scale segments");
+    static_assert((BM + 3 * BN) % 64 == 0, "64-float scale segments");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 };
 
@@ -142,7 +142,7 @@ __device__ __forceinline__ v4i expand_w4(v2u p)
                (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u), (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool DIV, int WB>
+template <int BM, int BN, int WM, int WN, int STAGES, bool DIV, int WB, bool POST>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     GemmProblem p, int tiles_m, int total_tiles)
 {
@@ -217,14 +217,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // load, so the first operand wait also covers them.
     const bool want_sx = L.out_kind != kOutI32;
     const bool has_sw = L.s_w != nullptr, has_bias = L.bias != nullptr;
+    const bool has_post = POST && L.post != 0;
     {
-        constexpr int kSeg = (BM + 2 * BN) / 64;
+        constexpr int kSeg = (BM + 3 * BN) / 64;
         const v4u sx_rsrc = buffer_rsrc(want_sx ? p.s_x + m0 : nullptr,
                                         want_sx ? (uint32_t)(a_rows * 4) : 0u);
         const v4u sw_rsrc = buffer_rsrc(has_sw ? L.s_w + n0 : nullptr,
                                         has_sw ? (uint32_t)(b_rows * 4) : 0u);
         const v4u bi_rsrc = buffer_rsrc(has_bias ? L.bias + n0 : nullptr,
                                         has_bias ? (uint32_t)(b_rows * 4) : 0u);
+        const v4u gt_rsrc = buffer_rsrc(has_post ? L.gate + n0 : nullptr,
+                                        has_post ? (uint32_t)(b_rows * 4) : 0u);
 #pragma unroll
         for (int q = 0; q < kSeg; ++q) {
             if (q % T::kWaves != wave)
@@ -236,8 +239,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             } else if (q < (BM + BN) / 64) {
                 if (has_sw)
                     dma_x1(sw_rsrc, 4 * lane, 256 * (q - BM / 64), dst);
-            } else if (has_bias) {
-                dma_x1(bi_rsrc, 4 * lane, 256 * (q - (BM + BN) / 64), dst);
+            } else if (q < (BM + 2 * BN) / 64) {
+                if (has_bias)
+                    dma_x1(bi_rsrc, 4 * lane, 256 * (q - (BM + BN) / 64), dst);
+            } else if (has_post) {
+                dma_x1(gt_rsrc, 4 * lane, 256 * (q - (BM + 2 * BN) / 64), dst);
             }
         }
     }
@@ -371,6 +377,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const bool full = (L.vec_store != 0) && (o + 4 <= N);
     const v4f sw = has_sw ? *reinterpret_cast<const v4f *>(sw_lds + cl) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
     const v4f bo = has_bias ? *reinterpret_cast<const v4f *>(b_lds + cl) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // gated residual (after the reconstruction, before the output cast)
+    const v4f gt = has_post ? *reinterpret_cast<const v4f *>(b_lds + BN + cl) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+    const float post_scale = L.post_scale;
+    const bool res_full = has_post && L.res_vec != 0 && (o + 4 <= N);
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -411,6 +421,44 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 if (has_bias)
                     x = x + bo[e];
                 t[e] = x;
+            }
+            if constexpr (POST) {
+                if (has_post) {
+                    // fl(fl(fl(y * scale) * gate) + residual), the residual in
+                    // the output dtype (bf16 widened exactly)
+                    float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if (kind == kOutF32) {
+                        const float *rp = static_cast<const float *>(L.residual) + r * L.ld_res + o;
+                        if (res_full) {
+                            const v4f q = *reinterpret_cast<const v4f *>(rp);
+                            rv[0] = q.x; rv[1] = q.y; rv[2] = q.z; rv[3] = q.w;
+                        } else {
+                            for (int e = 0; e < 4 && o + e < N; ++e)
+                                rv[e] = rp[e];
+                        }
+                    } else {
+                        const uint16_t *rp = static_cast<const uint16_t *>(L.residual) + r * L.ld_res + o;
+                        unsigned h[4] = {0u, 0u, 0u, 0u};
+                        if (res_full) {
+                            const v2u q = *reinterpret_cast<const v2u *>(rp);
+                            h[0] = q.x & 0xFFFFu; h[1] = q.x >> 16; h[2] = q.y & 0xFFFFu; h[3] = q.y >> 16;
+                        } else {
+                            for (int e = 0; e < 4 && o + e < N; ++e)
+                                h[e] = rp[e];
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            rv[e] = __builtin_bit_cast(float, h[e] << 16);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = t[e];
+                        if (post_scale != 1.0f)
+                            x = x * post_scale;
+                        x = x * gt[e];
+                        t[e] = x + rv[e];
+                    }
+                }
             }
             if (kind == kOutF32) {
                 float *y = static_cast<float *>(Yv) + r * ldy + o;
@@ -453,16 +501,22 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     }
     if (total == 0)
         return hipSuccess;
-    // the unscale division is compiled in only when some linear needs it
-    bool div = false;
-    for (int d = 0; d < p.n_lin; ++d)
+    // the unscale division and the gated residual are compiled in only when
+    // some linear needs them
+    bool div = false, post = false;
+    for (int d = 0; d < p.n_lin; ++d) {
         div = div || p.lin[d].alpha != 1.0f;
-    if (div)
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, true, WB>), dim3(total), dim3(T::kThreads),
-                           0, stream, p, tiles_m, total);
-    else
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, false, WB>), dim3(total), dim3(T::kThreads),
-                           0, stream, p, tiles_m, total);
+        post = post || p.lin[d].post != 0;
+    }
+#define CONVROT_GEMM(D, P)                                                                       \
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, D, WB, P>), dim3(total),         \
+                       dim3(T::kThreads), 0, stream, p, tiles_m, total)
+    if (post) {
+        if (div) CONVROT_GEMM(true, true); else CONVROT_GEMM(false, true);
+    } else {
+        if (div) CONVROT_GEMM(true, false); else CONVROT_GEMM(false, false);
+    }
+#undef CONVROT_GEMM
     return hipGetLastError();
 }
 
@@ -472,20 +526,24 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
 {
     // Large grids use 256 x 256 tiles computed by 16 waves (4 x 4, four per
     // SIMD, so that one wave's LDS and barrier waits are covered by the MFMAs
-    // of the others); grids too small to cover the 256 CUs with them fall
-    // back to 128 x 128 tiles with 8 waves (2 x 4; 64 KB of LDS, so two
-    // workgroups fit on a CU).  Both use a 4-stage ring: measured on gfx950,
-    // deeper rings (6 or 8 stages) were slower for every shape tried once
-    // they cost the second resident workgroup, and no faster otherwise.
+    // of the others); grids of fewer than 160 such tiles (under 62.5% of the
+    // 256 CUs for one round) use 128 x 128 tiles with 8 waves (2 x 4; 64 KB of
+    // LDS, so two workgroups fit on a CU).  Measured on gfx950 at K = 3072: a
+    // round of 256 x 256 tiles costs about the same for any count up to 256
+    // (192 tiles: 50 us against 59 us in 128 x 128 tiles; 96 tiles: 44 us
+    // against 34 us).  Both use a 4-stage ring: deeper rings (6 or 8 stages)
+    // were slower for every shape tried once they cost the second resident
+    // workgroup, and no faster otherwise.
     int64_t big = 0;
     for (int d = 0; d < p.n_lin; ++d)
         big += ((p.M + 255) / 256) * ((p.lin[d].N + 255) / 256);
+    constexpr int64_t kBigTiles = 160;
     if (p.w_bits == 4) {
-        if (big >= 256)
+        if (big >= kBigTiles)
             return launch_tiled<256, 256, 4, 4, 4, 4>(p, stream);
         return launch_tiled<128, 128, 2, 4, 4, 4>(p, stream);
     }
-    if (big >= 256)
+    if (big >= kBigTiles)
         return launch_tiled<256, 256, 4, 4, 4, 8>(p, stream);
     return launch_tiled<128, 128, 2, 4, 4, 8>(p, stream);
 }

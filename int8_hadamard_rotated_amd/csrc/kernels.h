@@ -41,6 +41,12 @@ struct GemmLinear {
     float alpha;         // divisor; 1 = none
     int out_kind;        // OutKind
     int vec_store;       // Y row starts allow 4-element vector stores
+    int post;            // 1: gated residual after the reconstruction
+    float post_scale;    // post: scalar multiply first (1 = none)
+    const float *gate;   // post: per-channel gate [N]
+    const void *residual;// post: [M][ld_res] in the output dtype (may equal Y exactly)
+    int64_t ld_res;
+    int res_vec;         // post: residual row starts allow 4-element vector loads
     int tiles_n;         // filled by the launcher
     int tile_begin;      // filled by the launcher: first linear tile index
 };

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
         "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
-        "int4_linear", "convrot_int4_gemm_i32"])
+        "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -172,6 +172,30 @@ def test_int4_linear_validation(lib):
     assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), 4, 132160, 4,
              ctypes.c_void_p(BASE + 2 * MB), None) == EOVF
     assert f(None, None, 0, 64, 4, None, None) == OK
+
+
+def test_post_validation(lib):
+    Y = BASE + 32 * MB
+
+    def lp(kind=cr.POST_GATED_RESIDUAL, scale=1.0, gate=BASE + 40 * MB, res=BASE + 44 * MB, ld=32,
+           M=8, N=32):
+        d = cr.PostDesc(kind, scale, gate, res, ld)
+        return lib.int8_linear_post(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + 8 * MB), M, 256,
+                                    ctypes.c_void_p(BASE + 16 * MB), None, None, N,
+                                    ctypes.c_float(1.0), ctypes.byref(d), ctypes.c_void_p(Y),
+                                    cr.F32, N, None)
+    assert lp(kind=5) == EUNSUP
+    assert lp(kind=5, M=0) == EUNSUP                     # checked before the empty-shape exit
+    assert lp(scale=float("inf")) == EINVAL
+    assert lp(gate=0) == EINVAL
+    assert lp(gate=BASE + 40 * MB + 2) == EINVAL
+    assert lp(res=0) == EINVAL
+    assert lp(res=BASE + 44 * MB + 2) == EINVAL          # f32 residual must be 4-byte aligned
+    assert lp(ld=16) == EINVAL                           # row stride below N
+    assert lp(res=Y + 16) == EOVL                        # overlaps Y without being Y
+    assert lp(res=Y, ld=48) == EOVL                      # Y's storage at another stride
+    assert lp(gate=Y + 64) == EOVL
+    assert lp(M=0) == OK
 
 
 def test_gemm_i32_validation(lib):

@@ -1,0 +1,89 @@
+"""The gated-residual epilogue (page "ggml operator extensions", section
+"sd.cpp integration": INT8 GEMM -> [Scale] -> Mul(gate) -> Add(residual))
+against the oracle's reconstruction followed by its gated residual, bit for
+bit (after the error gates of the linear tests)."""
+import numpy as np
+import pytest
+
+import int8_hadamard_rotated_amd as cr
+import oracle
+import workloads
+from gpu_util import THREADS, dev, dev_x, host, say
+from test_gpu_linear import check_y, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def case(rng, orc, M, K, N, G=64):
+    X = workloads.gaussian_activations(rng, M, K, 0.01, 30.0, workloads.F32)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+    p = orc.quantize_rows(X, G, threads=THREADS)
+    A = orc.gemm_i32(p.q, Qw, threads=THREADS)
+    gate = (rng.standard_normal(N) * 0.3).astype(np.float32)
+    return p, Qw, sw, b, A, gate
+
+
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+def test_gated_residual_bit_exact(orc, y_dtype):
+    import torch
+    rng = np.random.default_rng(71)
+    tdt = torch.float32 if y_dtype == oracle.F32 else torch.bfloat16
+    for (M, K, N) in ((129, 192, 250), (1024 + 3, 256, 4096 + 5)):
+        p, Qw, sw, b, A, gate = case(rng, orc, M, K, N)
+        R = workloads.gaussian_activations(rng, M, N, 0.0, 1.0,
+                                           workloads.F32 if y_dtype == oracle.F32 else workloads.BF16)
+        Yf = orc.epilogue(A, p.s, sw, b, 1.0, oracle.F32, threads=THREADS)
+        for scale in (1.0, 0.37):
+            want = orc.gated_residual(Yf, gate, R, scale, y_dtype, threads=THREADS)
+            say("gated residual", M, K, N, y_dtype, scale)
+            Rd = dev_x(R) if y_dtype == oracle.BF16 else dev(R)
+            Y = cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), 1.0,
+                                    cr.GatedResidual(dev(gate), Rd, scale), y_dtype=y_dtype)
+            check_y(host(Y), want, y_dtype, f"gated {M}x{K}x{N} scale={scale}")
+            # in place: the residual is the output tensor
+            say("gated residual in place", M, K, N, y_dtype, scale)
+            Yi = Rd.clone()
+            cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), 1.0,
+                                cr.GatedResidual(dev(gate), Yi, scale), Y=Yi)
+            check_y(host(Yi), want, y_dtype, f"gated in place {M}x{K}x{N} scale={scale}")
+
+
+def test_gated_residual_strided(orc):
+    """A residual with a row stride above N and an output with another one."""
+    import torch
+    rng = np.random.default_rng(72)
+    M, K, N = 70, 256, 61
+    p, Qw, sw, b, A, gate = case(rng, orc, M, K, N)
+    Rw = rng.standard_normal((M, N + 3)).astype(np.float32)
+    want = orc.gated_residual(orc.epilogue(A, p.s, sw, b), gate, np.ascontiguousarray(Rw[:, :N]))
+    big = torch.full((M, 67), -7.0, dtype=torch.float32, device="cuda:0")
+    say("gated strided")
+    cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), 1.0,
+                        cr.GatedResidual(dev(gate), dev(Rw)[:, :N]), Y=big[:, :N])
+    got = host(big)
+    check_y(np.ascontiguousarray(got[:, :N]), want, oracle.F32, "gated strided")
+    assert np.all(got[:, N:] == -7.0), "wrote past N"
+
+
+def test_gated_residual_workload(orc):
+    """The DiT output projection with its gated residual in place, at full
+    size from a GPU-quantized packed tensor, sampled rows."""
+    w = workloads.WORKLOADS["proj_gated"]
+    inp = workloads.make_inputs(w)
+    Qw, sw = orc.weight_prep(inp.W[0], w.G, threads=THREADS)
+    say("proj_gated")
+    packed = cr.convrot_quantize_rows(dev_x(inp.X), w.G)
+    qx, sx = cr.packed_parts(packed, w.M, w.K)
+    Y = dev_x(inp.residual)
+    cr.int8_linear_post(qx, sx, dev(Qw), dev(sw), dev(inp.b[0]), 1.0,
+                        cr.GatedResidual(dev(inp.gate), Y), Y=Y, M=w.M)
+    rows = sample_rows(w.M, 24, w.seed)
+    Yf = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[0], 1.0, oracle.F32, threads=THREADS)
+    want = orc.gated_residual(Yf, inp.gate, inp.residual[rows], 1.0, oracle.BF16, threads=THREADS)
+    check_y(np.ascontiguousarray(host(Y)[rows]), want, oracle.BF16, "proj_gated Y")

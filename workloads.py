@@ -25,6 +25,9 @@ Recipe, per workload (fixed draw order):
         W4_j = rng.integers(0, 256, (N, K/2), uint8)            # every nibble value
         s_w_j = exp(rng.uniform(log 1e-3, log 1e-2, N)) as float32
         b_j = rng.standard_normal(N, float32) * 0.1
+    when the workload has a gated-residual epilogue:
+        gate = rng.standard_normal(N, float32) * 0.3
+        residual = rng.standard_normal((M, N), float32), in the output dtype
     when the workload has a Modulate producer (per-channel vectors, as the
     adaLN modulation of a DiT block supplies them):
         scale = rng.standard_normal(K, float32) * 0.3
@@ -55,6 +58,7 @@ class Workload:
     outlier_f: float = 30.0
     modulate: bool = False            # a Modulate producer before the rotation
     w_bits: int = 8                   # 4: convrot_w4a4 packed weights
+    gated: bool = False               # a gated-residual epilogue after the linear
     note: str = ""
 
     @property
@@ -77,6 +81,9 @@ WORKLOADS = {
                            note="DiT MLP up-projection with its Modulate producer fused"),
     "mlp_up_w4": Workload("mlp_up_w4", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=6,
                           w_bits=4, note="DiT MLP up-projection with convrot_w4a4 weights"),
+    "proj_gated": Workload("proj_gated", 4096, 3072, 3072, 256, BF16, BF16, (1.0,), seed=7,
+                           gated=True,
+                           note="DiT output projection with its gated residual, in place"),
     "mlp_down": Workload("mlp_down", 16384, 12288, 3072, 256, BF16, BF16, (1.0,), seed=4,
                          note="batched MLP down-projection, 4 images x 4096 tokens, bf16 in/out"),
 }
@@ -127,6 +134,8 @@ class Inputs:
     s_w: list = field(default_factory=list) # float32 [N] per linear (4-bit weights only)
     mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
     mod_shift: np.ndarray | None = None     # float32 [K]
+    gate: np.ndarray | None = None          # float32 [N] (gated residual)
+    residual: np.ndarray | None = None      # [M,N] in the output dtype (gated residual)
 
 
 def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> Inputs:
@@ -149,6 +158,9 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
         inp.b.append(b)
     if w.modulate:
         inp.mod_scale, inp.mod_shift = modulation(rng, w.K)
+    if w.gated:
+        inp.gate = rng.standard_normal(w.N, dtype=np.float32) * np.float32(0.3)
+        inp.residual = gaussian_activations(rng, rows, w.N, 0.0, 1.0, w.y_dtype)
     return inp
 
 
