@@ -115,7 +115,8 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
 size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed);
 
 /* The fused layer for one linear: convrot_quantize_rows into the workspace,
- * then int8_linear on it.  workspace >= convrot_workspace_bytes(M, K, 1);
+ * then int8_linear on it (a power-of-two input scale is folded as in
+ * convrot_int8_linear_shared).  workspace >= convrot_workspace_bytes(M, K, 1);
  * contents are not preserved between calls.  Y may alias X (X is fully
  * consumed before Y is written) but not Qw, s_w, bias or the workspace. */
 int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -139,9 +140,20 @@ typedef struct {
  * gets one quantization pass (all alpha = 1 linears share one packed tensor,
  * as the page prescribes; linears with equal alpha != 1 also share, which
  * gives the same bits as separate passes); then one grouped GEMM launch per
- * packed tensor covers all linears that read it.  descs is host memory,
- * 1 <= n <= 16; workspace >= convrot_workspace_bytes(M, K, distinct scales).
- * Outputs must not overlap each other, any weight-side input or the workspace. */
+ * packed tensor covers all linears that read it.
+ *
+ * A power-of-two input scale 2^k with |k| <= 16 counts as alpha = 1: such a
+ * linear reads the alpha = 1 packed tensor and its reconstruction skips the
+ * division.  Multiplying by 2^k before the rotation and dividing by it after
+ * are both exact, and binary32 rounding commutes with the scaling, so the
+ * output bits are those of its own pass whenever the inputs meet the
+ * quantizer's contract (each |x| zero or in [2^-100, 2^100]) and the
+ * reconstruction's products stay in the normal range (an extension beyond
+ * the pages, which give every alpha != 1 its own pass).
+ *
+ * descs is host memory, 1 <= n <= 16; workspace >= convrot_workspace_bytes(M,
+ * K, number of distinct scales after that folding).  Outputs must not overlap
+ * each other, any weight-side input or the workspace. */
 int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                int group_size, int n, const convrot_linear_desc *descs,
                                void *workspace, size_t workspace_bytes, void *stream);

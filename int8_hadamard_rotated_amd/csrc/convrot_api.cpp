@@ -332,6 +332,23 @@ int gemm_i32_impl(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int6
     return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
+// Input scales 2^k with |k| <= 16 give the bits of the alpha = 1 pass: the
+// pre-scale by 2^k and the division by 2^k are both exact, and so is every
+// rounding in between (binary32 rounding commutes with scaling by a power of
+// two in the normal range, and the quantizer's input contract keeps every
+// rotation value that could round there).  Such linears read the alpha = 1
+// packed tensor and skip the division.
+constexpr int kFoldedScaleExp = 16;
+
+float quantize_scale_of(float input_scale)
+{
+    int e = 0;
+    if (input_scale > 0.0f && std::frexp(input_scale, &e) == 0.5f && e - 1 >= -kFoldedScaleExp &&
+        e - 1 <= kFoldedScaleExp)
+        return 1.0f;
+    return input_scale;
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,11 +417,12 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
                           true, &chk[i]);
         if (rc != CONVROT_OK)
             return rc;
+        const float a = quantize_scale_of(d.input_scale);
         int s = 0;
-        while (s < n_slots && scales[s] != d.input_scale)
+        while (s < n_slots && scales[s] != a)
             ++s;
         if (s == n_slots)
-            scales[n_slots++] = d.input_scale;
+            scales[n_slots++] = a;
         slot_of[i] = s;
     }
     if (M == 0)
@@ -454,7 +472,8 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
             if (slot_of[i] != s || descs[i].N == 0)
                 continue;
             const convrot_linear_desc &d = descs[i];
-            p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, d.input_scale, d.Y,
+            // the divisor is the scale of the pass this linear reads
+            p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, scales[s], d.Y,
                                            out_kind_of(d.y_dtype), d.ldy);
         }
         if (p.n_lin == 0)

@@ -122,6 +122,78 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
     return lo | hi;
 }
 
+// Span offset of chunk c of lane (j0, j1) in its quad (see the layout above).
+__device__ __forceinline__ int chunk_offset(int j0, int j1, int c)
+{
+    return 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
+}
+
+// The rotation of one quad span held in the quad layout: one H4 per base-4
+// digit of the in-group index, digit 0 first.
+template <int G, int NC>
+__device__ __forceinline__ void rotate_span(float (&v)[NC][8])
+{
+    // digit 0 (stride 1)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
+        h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
+    }
+    // digit 1 (stride 4): low bit p>>2, high bit lane bit 0
+    if constexpr (G >= 16) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                h4_split<kQuadPermXor1>(v[c][p], v[c][p + 4]);
+    }
+    // digit 2 (stride 16): low bit c&1, high bit lane bit 1
+    if constexpr (G >= 64) {
+#pragma unroll
+        for (int c = 0; c < NC; c += 2)
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                h4_split<kQuadPermXor2>(v[c][p], v[c + 1][p]);
+    }
+    // digit 3 (stride 64): chunk bits 1..2
+    if constexpr (G >= 256) {
+#pragma unroll
+        for (int c0 = 0; c0 < 2; ++c0)
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                h4_local(v[c0][p], v[c0 + 2][p], v[c0 + 4][p], v[c0 + 6][p]);
+    }
+}
+
+// max |y| over the quad's span, the same in all four lanes.
+template <int NC>
+__device__ __forceinline__ float quad_abs_max(const float (&v)[NC][8])
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            m = fmaxf(m, fabsf(v[c][p]));
+    m = fmaxf(m, quad_swap<kQuadPermXor1>(m));
+    return fmaxf(m, quad_swap<kQuadPermXor2>(m));
+}
+
+// Codes of one chunk: rne(fl(y * inv)) in two's complement, 8 bytes.
+__device__ __forceinline__ v2u encode8(const float (&v)[8], float inv)
+{
+    unsigned w[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const float t = v[p] * inv;
+        w[p] = __builtin_bit_cast(unsigned, t + 12582912.0f);
+    }
+    v2u out;
+    out.x = pack_low_bytes(w[0], w[1], w[2], w[3]);
+    out.y = pack_low_bytes(w[4], w[5], w[6], w[7]);
+    return out;
+}
+
 // Workgroup quad index -> (row within the workgroup, quad within the row).
 // Without a producer quads are row-major.  With the Modulate producer they
 // are column-major, so that the quads of one wave that read the same columns
@@ -209,46 +281,10 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
                     v[c][p] = v[c][p] * alpha;
         }
 
-        // digit 0 (stride 1)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
-            h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
-        }
-        // digit 1 (stride 4): low bit p>>2, high bit lane bit 0
-        if constexpr (G >= 16) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    h4_split<kQuadPermXor1>(v[c][p], v[c][p + 4]);
-        }
-        // digit 2 (stride 16): low bit c&1, high bit lane bit 1
-        if constexpr (G >= 64) {
-#pragma unroll
-            for (int c = 0; c < NC; c += 2)
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    h4_split<kQuadPermXor2>(v[c][p], v[c + 1][p]);
-        }
-        // digit 3 (stride 64): chunk bits 1..2
-        if constexpr (G >= 256) {
-#pragma unroll
-            for (int c0 = 0; c0 < 2; ++c0)
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    h4_local(v[c0][p], v[c0 + 2][p], v[c0 + 4][p], v[c0 + 6][p]);
-        }
+        rotate_span<G, NC>(v);
 
         // row max: lane, quad (DPP), then the row's quads (LDS)
-        float m = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-                m = fmaxf(m, fabsf(v[c][p]));
-        m = fmaxf(m, quad_swap<kQuadPermXor1>(m));
-        m = fmaxf(m, quad_swap<kQuadPermXor2>(m));
+        const float m = quad_abs_max<NC>(v);
         if ((tid & 3) == 0)
             atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
     }
@@ -272,18 +308,8 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
     if (q_in_row == 0 && (tid & 3) == 0)
         S[row] = __fdiv_rn(m, 127.0f);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        unsigned w[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const float t = v[c][p] * inv;
-            w[p] = __builtin_bit_cast(unsigned, t + 12582912.0f);
-        }
-        v2u out;
-        out.x = pack_low_bytes(w[0], w[1], w[2], w[3]);
-        out.y = pack_low_bytes(w[4], w[5], w[6], w[7]);
-        *reinterpret_cast<v2u *>(qr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1)) = out;
-    }
+    for (int c = 0; c < NC; ++c)
+        *reinterpret_cast<v2u *>(qr + chunk_offset(j0, j1, c)) = encode8(v[c], inv);
 }
 
 // ---- binary32 inputs: the same arithmetic with the row data staged in LDS.
@@ -385,40 +411,8 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
                 for (int p = 0; p < 8; ++p)
                     v[c][p] = v[c][p] * alpha;
         }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
-            h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
-        }
-        if constexpr (G >= 16) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    h4_split<kQuadPermXor1>(v[c][p], v[c][p + 4]);
-        }
-        if constexpr (G >= 64) {
-#pragma unroll
-            for (int c = 0; c < NC; c += 2)
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    h4_split<kQuadPermXor2>(v[c][p], v[c + 1][p]);
-        }
-        if constexpr (G >= 256) {
-#pragma unroll
-            for (int c0 = 0; c0 < 2; ++c0)
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    h4_local(v[c0][p], v[c0 + 2][p], v[c0 + 4][p], v[c0 + 6][p]);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-                m = fmaxf(m, fabsf(v[c][p]));
-        m = fmaxf(m, quad_swap<kQuadPermXor1>(m));
-        m = fmaxf(m, quad_swap<kQuadPermXor2>(m));
+        rotate_span<G, NC>(v);
+        const float m = quad_abs_max<NC>(v);
         if ((tid & 3) == 0)
             atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
     }
@@ -444,17 +438,8 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
                 S[row] = __fdiv_rn(m, 127.0f);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                unsigned w[8];
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const float t = v[c][p] * inv;
-                    w[p] = __builtin_bit_cast(unsigned, t + 12582912.0f);
-                }
-                v2u out;
-                out.x = pack_low_bytes(w[0], w[1], w[2], w[3]);
-                out.y = pack_low_bytes(w[4], w[5], w[6], w[7]);
-                const int o = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
-                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = out;
+                const int o = chunk_offset(j0, j1, c);
+                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = encode8(v[c], inv);
             }
         }
     }

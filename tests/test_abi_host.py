@@ -225,12 +225,18 @@ def shared(lib, ds, ws=BASE + 512 * MB, ws_bytes=1 << 30, M=8, K=256, X=BASE, G=
 def test_shared_validation(lib):
     W1, W2 = BASE + 64 * MB, BASE + 96 * MB
     Y1, Y2 = BASE + 128 * MB, BASE + 160 * MB
-    good = [desc(W1, Y1), desc(W2, Y2, a=0.5)]
+    good = [desc(W1, Y1), desc(W2, Y2, a=0.3)]
     need = cr.convrot_workspace_bytes(8, 256, 2)
+    need1 = cr.convrot_workspace_bytes(8, 256, 1)
     assert shared(lib, []) == EINVAL
     assert shared(lib, [desc(W1, Y1)] * 17) == EINVAL
     assert shared(lib, good, ws=0) == EWS
     assert shared(lib, good, ws_bytes=need - 1) == EWS
+    # a power-of-two input scale 2^k, |k| <= 16, reads the alpha = 1 packed
+    # tensor, 2^17 needs a slot of its own (every call here fails validation
+    # before any HIP call; the GPU tests run the passing case)
+    assert shared(lib, [desc(W1, Y1), desc(W2, Y2, a=0.5)], ws_bytes=need1 - 1) == EWS
+    assert shared(lib, [desc(W1, Y1), desc(W2, Y2, a=2.0 ** 17)], ws_bytes=need1) == EWS
     assert shared(lib, [desc(W1, Y1), desc(W2, Y1 + 64)]) == EOVL          # outputs overlap
     assert shared(lib, [desc(W1, Y1), desc(W2, W1 + 128)]) == EOVL         # output hits a weight
     assert shared(lib, good, ws=Y1) == EOVL                                 # workspace hits an output

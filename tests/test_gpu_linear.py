@@ -154,6 +154,32 @@ def test_shared_qkv(orc):
     assert_bits_equal(outs[3], one, "input scale 0.5 vs 1")
 
 
+def test_shared_power_of_two_scales(orc):
+    """Input scales 2^k (|k| <= 16) read the alpha = 1 packed tensor and skip
+    the division; every output must still equal the oracle's literal path
+    (pre-scale, own quantization, division) bit for bit.  Six linears need
+    three packed tensors: {1, 0.5, 4, 2^-16}, {2^17} and {0.3}."""
+    import torch
+    rng = np.random.default_rng(41)
+    M, K, G = 257, 768, 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    scales = [1.0, 0.5, 4.0, 2.0 ** -16, 2.0 ** 17, 0.3]
+    Ns = [96, 64, 130, 32, 80, 17]
+    Xd = dev_x(X)
+    preps, lins = [], []
+    for a, N in zip(scales, Ns):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        preps.append((Qw, sw, b))
+        lins.append(dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=oracle.BF16))
+    ws = torch.empty(cr.convrot_workspace_bytes(M, K, 3), dtype=torch.uint8, device="cuda:0")
+    say("shared power-of-two scales")
+    outs = [host(y) for y in cr.convrot_int8_linear_shared(Xd, G, lins, workspace=ws)]
+    for (Qw, sw, b), a, y in zip(preps, scales, outs):
+        want = orc.linear(X, G, Qw, sw, b, a, oracle.BF16, threads=THREADS)
+        check_y(y, want, oracle.BF16, f"alpha={a}")
+
+
 def test_fused_output_may_alias_input(orc):
     import torch
     rng = np.random.default_rng(12)

@@ -34,9 +34,14 @@ def test_workload_packed_bit_exact(orc, name):
         assert_bits_equal(got, want, f"{name} packed (alpha={alpha})")
 
 
-# K = 4096 and 8192 fill a 256-thread workgroup (4 waves) of the staged binary32 kernel
-EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (129, 3072), (9, 4096),
-               (6, 8192), (7, 12288), (2, 65536)]
+# K = 4096 and 8192 fill a 256-thread workgroup (4 waves) of the staged binary32 kernel.
+# bf16 rows with K % 256 == 0 whose rows fill 1, 2 or 3 passes of 16 quads run
+# whole rows per wave: 16 rows per wave (K = 256, 768), 8 (512, 1536), 4 (3072),
+# 2 (6144) and 1 (4096, 8192, 12288); K = 1280 and 65536 do not fit and take the
+# workgroup kernel.
+EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (13, 512), (17, 768),
+               (33, 1280), (11, 1536), (129, 3072), (9, 4096), (3, 6144), (6, 8192), (7, 12288),
+               (2, 65536)]
 
 
 @pytest.mark.parametrize("G", [4, 16, 64, 256])
@@ -76,12 +81,16 @@ def test_special_rows(orc):
             np.where(np.arange(K) == 77, 1000.0, 0.0).astype(np.float32),
             -tie]
     X = np.stack(rows)
+    Xb = workloads.f32_to_bf16_bits(X)
     for G in (4, 16, 64, 256):
         for alpha in (1.0, 0.5):
             say("special rows", G, alpha)
             got = gpu_packed(X, G, alpha)
             want = orc.quantize_rows(X, G, alpha).raw
             assert_bits_equal(got, want, f"special rows G={G} alpha={alpha}")
+            say("special rows bf16", G, alpha)
+            assert_bits_equal(gpu_packed(Xb, G, alpha), orc.quantize_rows(Xb, G, alpha).raw,
+                              f"special bf16 rows G={G} alpha={alpha}")
     # the tie row itself against the golden codes (G = 16 leaves it unrotated)
     p = oracle.Packed(gpu_packed(X, 16), X.shape[0], K)
     assert np.array_equal(p.q[1], np.repeat(codes, 16))
