@@ -60,13 +60,21 @@ struct Tile {
     static constexpr int kDmaA = BM / 16, kDmaB = BN / kRowsPerDmaB;
     static constexpr int kDma = kDmaA + kDmaB;             // DMA instructions per step
     static constexpr int kLoads = (kDma + kWaves - 1) / kWaves;   // at most, per wave per step
-    static constexpr int kScaleOff = kStages * kStageBytes;    // s_x [BM], s_w, bias, gate [BN]
+    // 4-bit weights: two slots of expanded B rows (64 bytes each, the int8
+    // layout) after the ring; each step's packed rows are expanded once
+    static constexpr int kExpOff = kStages * kStageBytes;
+    static constexpr int kExpSlot = WB == 4 ? BN * kBK : 0;
+    static constexpr int kScaleOff = kExpOff + 2 * kExpSlot;  // s_x [BM], s_w, bias, gate [BN]
     static constexpr int kLdsBytes = kScaleOff + 4 * (BM + 3 * BN);
+    // steps whose DMA must have landed beyond the next one at an iteration's
+    // top: 4-bit weights expand the step after next there
+    static constexpr int kAhead = WB == 4 ? 1 : 0;
     static_assert(WB == 8 || WB == 4, "weight bits");
     static_assert(BN % kRowsPerDmaB == 0, "whole B DMA blocks");
     static_assert(BM % 16 == 0 && kWaveM % 16 == 0 && kWaveN % 16 == 0, "");
     static_assert(kLoads <= kTM, "at most one DMA load per MFMA group");
-    static_assert(STAGES >= 4, "ring depth");
+    static_assert(STAGES >= 4 + kAhead, "ring depth");
+    static_assert(WB == 8 || BN == 16 * kWaves, "one packed 8-byte chunk per lane and step");
     static_assert((BM + 3 * BN) % 64 == 0, "64-float scale segments");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 };
@@ -177,10 +185,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // (64 bytes each, or 32 for packed 4-bit weights).  A DMA instruction moves
     // 1 KB: A instruction g moves rows 16 g .. 16 g + 15 (lane L writes row
     // 16 g + L/4, slot L%4, which receives logical K chunk (L%4) ^ swz(row));
-    // a 4-bit B instruction moves 32 rows of 32 bytes (lane L writes row L/2,
-    // half L%2, which receives logical half (L%2) ^ (row bit 3)).  The
-    // swizzles only depend on row bits below the block size, so one per-lane
-    // offset serves every instruction.  Wave w issues instructions
+    // a 4-bit B instruction moves 32 packed rows of 32 bytes (lane L writes
+    // row L/2, half L%2).  The swizzle only depends on row bits below the
+    // block size, so one per-lane offset serves every instruction.  Wave w issues instructions
     // g = kWaves * q + w (g < kDma), one per MFMA group.
     //
     // Each operand tile is addressed through a buffer descriptor that starts
@@ -193,8 +200,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const v4u b_rsrc = buffer_rsrc(L.Qw + n0 * kb, (uint32_t)(b_rows * kb));
     const int ld_row = lane >> 2;
     const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
-    const int ld_voff_b = WB == 4 ? (lane >> 1) * (int)kb + 16 * ((lane & 1) ^ ((lane >> 4) & 1))
-                                  : ld_voff;
+    const int ld_voff_b = WB == 4 ? (lane >> 1) * (int)kb + 16 * (lane & 1) : ld_voff;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t *)lds;
     // DMA instructions this wave issues per step
     const int my_loads = (T::kDma - wave + T::kWaves - 1) / T::kWaves;
@@ -260,22 +266,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int frag_row = lane & 15, frag_chunk = lane >> 4;
     const int frag_slot = 16 * (frag_chunk ^ swz(frag_row));
     const int a_frag0 = (wm * T::kWaveM + frag_row) * T::kStride + frag_slot;
-    // 4-bit B rows: lane l reads the 8 packed bytes of logical K chunk l/16,
-    // stored at 8-byte slot (l/16) ^ (2 * row bit 3) of its 32-byte row
-    const int b_frag0 = WB == 4 ? T::kABytes + (wn * T::kWaveN + frag_row) * T::kStrideB +
-                                      8 * (frag_chunk ^ (2 * ((frag_row >> 3) & 1)))
-                                : T::kABytes + (wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
-    auto read_a = [&](int stage, int i) {
-        return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + a_frag0 +
+    // B fragments come from the ring (int8 weights) or from the expanded
+    // slots (4-bit weights), both in the int8 row layout
+    const int b_frag0 = (wn * T::kWaveN + frag_row) * T::kStride + frag_slot;
+    auto read_a = [&](int step, int i) {
+        return *reinterpret_cast<const v4i *>(lds + (step % T::kStages) * T::kStageBytes + a_frag0 +
                                               i * 16 * T::kStride);
     };
-    auto read_b = [&](int stage, int j) {
-        if constexpr (WB == 4)
-            return expand_w4(*reinterpret_cast<const v2u *>(lds + stage * T::kStageBytes + b_frag0 +
-                                                            j * 16 * T::kStrideB));
-        else
-            return *reinterpret_cast<const v4i *>(lds + stage * T::kStageBytes + b_frag0 +
-                                                  j * 16 * T::kStride);
+    auto read_b = [&](int step, int j) {
+        const int base = WB == 4 ? T::kExpOff + (step & 1) * T::kExpSlot
+                                 : (step % T::kStages) * T::kStageBytes + T::kABytes;
+        return *reinterpret_cast<const v4i *>(lds + base + b_frag0 + j * 16 * T::kStride);
+    };
+    // 4-bit expansion: lane l of wave w takes packed row 16 w + l/4, 8-byte
+    // chunk l%4 (logical 16-byte K chunk l%4 of the expanded row)
+    const int ex_row = 16 * wave + (lane >> 2), ex_chunk = lane & 3;
+    const int ex_src = T::kABytes + ex_row * T::kStrideB + 8 * ex_chunk;
+    const int ex_dst = T::kExpOff + ex_row * T::kStride + 16 * (ex_chunk ^ swz(ex_row));
+    auto read_packed = [&](int step) {
+        return *reinterpret_cast<const v2u *>(lds + (step % T::kStages) * T::kStageBytes + ex_src);
+    };
+    auto write_expanded = [&](int step, v2u pk) {
+        *reinterpret_cast<v4i *>(lds + ex_dst + (step & 1) * T::kExpSlot) = expand_w4(pk);
     };
 
     // ---- main loop, software-pipelined one K-step ahead on fragments.
@@ -290,19 +302,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // k + S - 1 (S = ring depth), spread one per MFMA group, may overwrite
     // stage (k-1) % S: loads are issued S - 2 iterations before the barrier
     // that needs them.
+    //
+    // 4-bit weights (kAhead = 1): the barrier at the top of iteration k also
+    // certifies step k+2's DMA; each lane then expands its packed chunk of
+    // step k+2 into expanded slot k % 2, whose step-k fragments were read in
+    // iteration k-1, and the barrier at the top of iteration k+1 publishes
+    // it before step k+2's fragments are read.  Steps 0 and 1 are expanded
+    // before the loop.  The ring keeps the same two iterations of DMA
+    // lookahead with one more stage.
     constexpr int S = T::kStages;
+    constexpr int AH = T::kAhead;
     static_assert((S - 2) * T::kLoads < 64, "vmcnt range");
     v4i fa[T::kTM], fb[T::kTN];
     const int ksteps = (int)(K / kBK);
     auto iteration = [&](int k) {
         const bool has_next = k + 1 < ksteps;
+        const bool expand = WB == 4 && k + 2 < ksteps;
         if (has_next) {
-            // step k+1 must have landed; steps k+2 .. k+S-2 may stay in flight
-            const int younger = (ksteps - k - 2) < (S - 3) ? (ksteps - k - 2) : (S - 3);
-            wait_vmcnt_le<(S - 3) * T::kLoads>(younger * my_loads);
+            // steps up to k+1+AH must have landed; k+2+AH .. k+S-2 may stay in flight
+            int younger = ksteps - k - 2 - AH;
+            younger = younger < S - 3 - AH ? younger : S - 3 - AH;
+            younger = younger > 0 ? younger : 0;
+            wait_vmcnt_le<(S - 3 - AH) * T::kLoads>(younger * my_loads);
             __syncthreads();
         }
-        const int next_stage = (k + 1) % S;
+        v2u pk{0u, 0u};
+        if constexpr (WB == 4) {
+            if (expand)
+                pk = read_packed(k + 2);
+        }
         const int dma_step = k + S - 1;
         const bool dma = dma_step < ksteps;
 #pragma unroll
@@ -310,14 +338,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             __builtin_amdgcn_sched_barrier(0);
             if (dma && i < T::kLoads)
                 issue_one(dma_step, i);
+            if constexpr (WB == 4) {
+                if (i == (T::kTM > 1 ? 1 : 0) && expand)
+                    write_expanded(k + 2, pk);
+            }
 #pragma unroll
             for (int j = 0; j < T::kTN; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
                 if (i == T::kTM - 1 && has_next)
-                    fb[j] = read_b(next_stage, j);
+                    fb[j] = read_b(k + 1, j);
             }
             if (has_next)
-                fa[i] = read_a(next_stage, i);
+                fa[i] = read_a(k + 1, i);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -329,11 +361,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             for (int q = 0; q < T::kLoads; ++q)
                 issue_one(s0, q);
     {
-        // step 0 must have landed (and the older scale loads)
-        const int younger = (ksteps - 1) < (S - 2) ? (ksteps - 1) : (S - 2);
-        wait_vmcnt_le<(S - 2) * T::kLoads>(younger * my_loads);
+        // steps 0 .. AH must have landed (and the older scale loads)
+        int younger = (ksteps < S - 1 ? ksteps : S - 1) - 1 - AH;
+        younger = younger > 0 ? younger : 0;
+        wait_vmcnt_le<(S - 2 - AH) * T::kLoads>(younger * my_loads);
     }
     __syncthreads();
+    if constexpr (WB == 4) {
+        write_expanded(0, read_packed(0));
+        if (ksteps > 1)
+            write_expanded(1, read_packed(1));
+        __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i)
         fa[i] = read_a(0, i);
@@ -531,7 +570,8 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
     // LDS, so two workgroups fit on a CU).  Measured on gfx950 at K = 3072: a
     // round of 256 x 256 tiles costs about the same for any count up to 256
     // (192 tiles: 50 us against 59 us in 128 x 128 tiles; 96 tiles: 44 us
-    // against 34 us).  Both use a 4-stage ring: deeper rings (6 or 8 stages)
+    // against 34 us).  Both use a 4-stage ring (5 with 4-bit weights, which
+    // expand a step ahead): deeper rings (6 or 8 stages)
     // were slower for every shape tried once they cost the second resident
     // workgroup, and no faster otherwise.
     int64_t big = 0;
@@ -540,8 +580,8 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
     constexpr int64_t kBigTiles = 160;
     if (p.w_bits == 4) {
         if (big >= kBigTiles)
-            return launch_tiled<256, 256, 4, 4, 4, 4>(p, stream);
-        return launch_tiled<128, 128, 2, 4, 4, 4>(p, stream);
+            return launch_tiled<256, 256, 4, 4, 5, 4>(p, stream);
+        return launch_tiled<128, 128, 2, 4, 5, 4>(p, stream);
     }
     if (big >= kBigTiles)
         return launch_tiled<256, 256, 4, 4, 4, 8>(p, stream);
