@@ -10,6 +10,12 @@ kernels.  For the shared QKV workload a step is one convrot_int8_linear_shared
 call.  After the timed steps each kernel is timed on its own (K back-to-back
 launches between two HIP events) for the roofline figures.
 
+Warm-up is W steps and at least --warmup-ms of wall time: a GPU that starts
+from idle runs these kernels boosted for about 2 ms, then throttles below its
+power-limited steady state and recovers over some 20 ms (kernel traces show the
+GEMM at 150, then 200, then 150 us), and the timed steps are meant to see the
+steady state.
+
 Inputs are seeded synthetic DiT-shaped tensors (workloads.py), resident in
 HBM before timing starts.  Several input sets are rotated across steps so that
 the activations of a step are not still held in the 256 MiB Infinity Cache
@@ -174,8 +180,14 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="after the W warm-up steps, keep stepping (untimed) until this much "
+                         "wall time has passed since the warm-up began: a GPU that starts "
+                         "from idle boosts for about 2 ms, then throttles below its "
+                         "power-limited steady state and takes some 20 ms to recover, so "
+                         "timed steps that begin earlier measure that transient")
     ap.add_argument("--workload", default="mlp_up", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated over steps (0: enough to exceed the Infinity Cache)")
@@ -277,9 +289,16 @@ def main() -> int:
             gemm(i)
 
     views = [cr.packed_parts(ws, w.M, w.K) for _, ws, _ in sets]
+    t_warm = time.perf_counter()
     for i in range(args.warmup):
         step(i)
+    warm_steps = args.warmup
     torch.cuda.synchronize()
+    while (time.perf_counter() - t_warm) * 1e3 < args.warmup_ms:
+        for _ in range(16):
+            step(warm_steps)
+            warm_steps += 1
+        torch.cuda.synchronize()
 
     # timed region: K whole steps, HIP events only at its two ends (an event
     # recorded between kernels leaves the GPU idle for a few microseconds)
@@ -315,6 +334,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -104,6 +104,10 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with int8_hadamard_rotated_amd._build.build()"
                            " (or __graft_entry__.build()); there is no fallback path")
+    # torch first: the library must bind the HIP runtime torch already holds
+    # (its own copy); loaded first, it would bind the system copy, and
+    # launches on torch's streams would then fail
+    _torch()
     lib = ctypes.CDLL(path)
     i64, i32, f32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     sigs = {

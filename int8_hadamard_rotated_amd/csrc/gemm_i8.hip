@@ -502,7 +502,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             if (kind == kOutF32) {
                 float *y = static_cast<float *>(Yv) + r * ldy + o;
                 if (full) {
-                    *reinterpret_cast<v4f *>(y) = v4f{t[0], t[1], t[2], t[3]};
+                    __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
                 } else {
                     for (int e = 0; e < 4 && o + e < N; ++e)
                         y[e] = t[e];
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
                 uint16_t *y = static_cast<uint16_t *>(Yv) + r * ldy + o;
                 if (full) {
-                    *reinterpret_cast<v2u *>(y) = v2u{w0, w1};
+                    __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u *>(y));
                 } else {
                     const unsigned ws[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
                     for (int e = 0; e < 4 && o + e < N; ++e)
