@@ -414,12 +414,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int64_t o = n0 + cl;
     const bool col_any = o < N;
     const bool full = (L.vec_store != 0) && (o + 4 <= N);
+    // A missing weight scale multiplies by 1 and a missing bias adds -0: both
+    // leave every binary32 value unchanged, zeros and their signs included,
+    // so the operations need no per-element selects.
     const v4f sw = has_sw ? *reinterpret_cast<const v4f *>(sw_lds + cl) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
-    const v4f bo = has_bias ? *reinterpret_cast<const v4f *>(b_lds + cl) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    const v4f bo = has_bias ? *reinterpret_cast<const v4f *>(b_lds + cl) : v4f{-0.0f, -0.0f, -0.0f, -0.0f};
     // gated residual (after the reconstruction, before the output cast)
     const v4f gt = has_post ? *reinterpret_cast<const v4f *>(b_lds + BN + cl) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
     const float post_scale = L.post_scale;
     const bool res_full = has_post && L.res_vec != 0 && (o + 4 <= N);
+    // Addresses: one per-lane element offset of the lane's first row, plus a
+    // uniform multiple of the row pitch per slot (scalar arithmetic), so that
+    // no slot repeats 64-bit multiplies; rows are checked against the tile's
+    // valid row count in 32 bits.
+    const int rows_valid = (int)a_rows;
+    const int lane_row0 = wm * T::kWaveM + rr0;                 // tile row of slot (0, 0)
+    int64_t y_lane = (m0 + lane_row0) * ldy + o;                // element offset in Y
+    int64_t r_lane = has_post ? (m0 + lane_row0) * L.ld_res + o : 0;
+    // opaque, so that the compiler does not fold the per-slot offsets back
+    // into per-slot 64-bit products
+    asm volatile("" : "+v"(y_lane));
+    asm volatile("" : "+v"(r_lane));
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -434,11 +449,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             const int rr = rr0 + kRowStep * sl;
             const v4i a = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cq);
             const int rl = wm * T::kWaveM + i * 16 + rr;        // row within the tile
-            const int64_t r = m0 + rl;
-            if (r >= M || !col_any)
+            if (rl >= rows_valid || !col_any)
                 continue;
+            const int dr = i * 16 + kRowStep * sl;              // rows below the lane's first
+            const int64_t y_off = y_lane + (int64_t)dr * ldy;
             if (kind == kOutI32) {
-                int32_t *y = static_cast<int32_t *>(Yv) + r * ldy + o;
+                int32_t *y = static_cast<int32_t *>(Yv) + y_off;
                 if (full) {
                     *reinterpret_cast<v4i *>(y) = a;
                 } else {
@@ -453,12 +469,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             for (int e = 0; e < 4; ++e) {
                 float x = (float)a[e];
                 x = x * sxr;
-                if (has_sw)
-                    x = x * sw[e];
+                x = x * sw[e];
                 if constexpr (DIV)
                     x = __fdiv_rn(x, alpha);
-                if (has_bias)
-                    x = x + bo[e];
+                x = x + bo[e];
                 t[e] = x;
             }
             if constexpr (POST) {
@@ -467,7 +481,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     // the output dtype (bf16 widened exactly)
                     float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                     if (kind == kOutF32) {
-                        const float *rp = static_cast<const float *>(L.residual) + r * L.ld_res + o;
+                        const float *rp = static_cast<const float *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
                         if (res_full) {
                             const v4f q = *reinterpret_cast<const v4f *>(rp);
                             rv[0] = q.x; rv[1] = q.y; rv[2] = q.z; rv[3] = q.w;
@@ -476,7 +490,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                                 rv[e] = rp[e];
                         }
                     } else {
-                        const uint16_t *rp = static_cast<const uint16_t *>(L.residual) + r * L.ld_res + o;
+                        const uint16_t *rp = static_cast<const uint16_t *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
                         unsigned h[4] = {0u, 0u, 0u, 0u};
                         if (res_full) {
                             const v2u q = *reinterpret_cast<const v2u *>(rp);
@@ -500,7 +514,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 }
             }
             if (kind == kOutF32) {
-                float *y = static_cast<float *>(Yv) + r * ldy + o;
+                float *y = static_cast<float *>(Yv) + y_off;
                 if (full) {
                     __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
                 } else {
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 // vector is miscompiled by this toolchain.
                 const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
                 const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
-                uint16_t *y = static_cast<uint16_t *>(Yv) + r * ldy + o;
+                uint16_t *y = static_cast<uint16_t *>(Yv) + y_off;
                 if (full) {
                     __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u *>(y));
                 } else {

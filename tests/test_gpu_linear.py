@@ -209,6 +209,32 @@ def test_empty_shapes(orc):
     assert Y.shape == (0, 8)
 
 
+def test_signed_zero_outputs(orc):
+    """Zero rows (A = 0) against negative weight scales give -0 before the
+    bias; without a bias the output must keep that sign, with one it must be
+    the bias (the oracle skips the missing operations)."""
+    rng = np.random.default_rng(32)
+    M, K, N = 12, 256, 40
+    Qx = workloads.random_codes(rng, (M, K))
+    Qx[3] = 0
+    Qx[7] = 0
+    Qw = workloads.random_codes(rng, (N, K))
+    sx = workloads.random_scales(rng, M)
+    sw = -workloads.random_scales(rng, N)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    A = orc.gemm_i32(Qx, Qw)
+    for y_dtype in (oracle.F32, oracle.BF16):
+        for bias in (None, b):
+            say("signed zeros", y_dtype, bias is None)
+            want = orc.epilogue(A, sx, sw, bias, 1.0, y_dtype)
+            got = host(cr.int8_linear(dev(Qx), dev(sx), dev(Qw), dev(sw),
+                                      None if bias is None else dev(bias), 1.0, y_dtype=y_dtype))
+            assert_bits_equal(got, want, f"signed zeros dtype={y_dtype} bias={bias is not None}")
+            if bias is None:
+                zero_bits = want[3].view(np.uint32 if y_dtype == oracle.F32 else np.uint16)
+                assert np.all(zero_bits == (0x80000000 if y_dtype == oracle.F32 else 0x8000))
+
+
 def test_bf16_output_subnormal_range(orc):
     """Outputs around the binary32 / bf16 subnormal boundary: the kernel's bf16
     conversion must round exactly like the oracle's (nearest, ties to even)."""
