@@ -47,6 +47,14 @@
  *     length K shared by every row: (x + x * scale) + shift, three separately
  *     rounded operations, the shift being optional.  Its binary32 output is
  *     the input of the quantizer above.
+ *   - RMSNorm -> Mul(weight) ahead of the Modulate producer (same page and
+ *     section, the RMSNorm -> Mul(weight) -> Mul(modulation) -> Add ->
+ *     Add(shift) -> ConvRot fusion; the page does not spell out RMSNorm's
+ *     arithmetic): per row, the squares fl(x * x) are summed pairwise within
+ *     each block of 64 consecutive features (adjacent pairs, then pairs of
+ *     those sums, ...) and the K/64 block sums are added left to right; then
+ *     mean = fl(S / K), d = fl(sqrt(fl(mean + eps))), r = fl(1 / d) (each
+ *     correctly rounded), y = fl(x * r) and, with a weight, fl(y * w[i]).
  */
 #include <math.h>
 #include <stdint.h>
@@ -278,6 +286,55 @@ int oracle_modulate_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64
             float y = x + xs;
             if (shift)
                 y = y + shift[i];
+            Y[r * K + i] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * RMSNorm -> Mul(weight) (page "ggml operator extensions", section "sd.cpp
+ * integration", the fusion chain that starts RMSNorm -> Mul(weight) and ends
+ * in ConvRot), in the reading stated at the top of this file.  weight may be
+ * NULL (no multiplication).  K must be a multiple of 64.  Y is binary32
+ * [M][K], contiguous.
+ */
+static float pairwise_sum64(const float *q)
+{
+    float t[64];
+    memcpy(t, q, sizeof t);
+    for (int n = 64; n > 1; n /= 2)
+        for (int i = 0; i < n / 2; ++i)
+            t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+int oracle_rmsnorm_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, float eps,
+                        const float *weight, float *Y, int threads)
+{
+    if (!X || !Y || M < 0 || K < 64 || K % 64 != 0 || ldx < K || !(eps >= 0.0f) || isinf(eps))
+        return ORACLE_EINVAL;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_EUNSUPPORTED;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t r = 0; r < M; ++r) {
+        float sq[64];
+        float S = 0.0f;
+        for (int64_t b = 0; b < K; b += 64) {
+            for (int i = 0; i < 64; ++i) {
+                const float x = load_widened(X, x_dtype, r * ldx + b + i);
+                sq[i] = x * x;
+            }
+            const float block = pairwise_sum64(sq);
+            S = b == 0 ? block : S + block;
+        }
+        const float mean = S / (float)K;
+        const float d = sqrtf(mean + eps);
+        const float rs = 1.0f / d;
+        for (int64_t i = 0; i < K; ++i) {
+            float y = load_widened(X, x_dtype, r * ldx + i) * rs;
+            if (weight)
+                y = y * weight[i];
             Y[r * K + i] = y;
         }
     }

@@ -421,6 +421,105 @@ def pin_modulate_special_cases(o):
     assert np.array_equal(o.modulate_rows(wide, sc, K=K), o.modulate_rows(X, sc))
 
 
+def sqrt_rn_f32(q: Fraction) -> Fraction:
+    """The binary32 value nearest to sqrt(q) (q >= 0 rational), ties to even:
+    the candidate whose rounding interval holds sqrt(q), decided by comparing
+    q with the squares of the interval ends exactly."""
+    if q == 0:
+        return Fraction(0)
+    c = np.float32(math.sqrt(float(q)))
+    for cand in (np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))):
+        v = F(cand)
+        lo = (v + F(np.nextafter(cand, np.float32(0)))) / 2
+        hi = (v + F(np.nextafter(cand, np.float32(np.inf)))) / 2
+        even = (int(np.float32(cand).view(np.uint32)) & 1) == 0
+        if (lo * lo < q or (lo * lo == q and even)) and (q < hi * hi or (q == hi * hi and even)):
+            return v
+    raise AssertionError("no candidate holds the root")
+
+
+def rmsnorm_exact(xw: np.ndarray, eps: float, w) -> list:
+    """One row of RMSNorm -> Mul(weight) in exact rationals, rounded to
+    binary32 after every operation, in the reading's order: pairwise sums of
+    the squares inside 64-feature blocks, block sums left to right."""
+    K = len(xw)
+    S = None
+    for b in range(0, K, 64):
+        t = [rne_f32(F(x) * F(x)) for x in xw[b:b + 64]]
+        while len(t) > 1:
+            t = [rne_f32(t[2 * i] + t[2 * i + 1]) for i in range(len(t) // 2)]
+        S = t[0] if S is None else rne_f32(S + t[0])
+    mean = rne_f32(S / K)
+    d = sqrt_rn_f32(rne_f32(mean + F(np.float32(eps))))
+    r = rne_f32(1 / d)
+    out = []
+    for i, x in enumerate(xw):
+        y = rne_f32(F(x) * r)
+        if w is not None:
+            y = rne_f32(y * F(w[i]))
+        out.append(y)
+    return out
+
+
+def pin_rmsnorm_exact(o):
+    """RMSNorm -> Mul(weight) against exact rational arithmetic with binary32
+    rounding (and a correctly rounded square root) at each step, for binary32
+    and bf16 rows, with and without the weight (page "ggml operator
+    extensions", the RMSNorm -> Mul(weight) -> ... -> ConvRot chain)."""
+    rng = np.random.default_rng(46)
+    M, K = 2, 192
+    X = workloads.gaussian_activations(rng, M, K, 0.05, 20.0, workloads.F32)
+    w = (1.0 + rng.standard_normal(K) * 0.2).astype(np.float32)
+    Xb = workloads.f32_to_bf16_bits(X)
+    for src, xw in ((X, X), (Xb, workloads.bf16_bits_to_f32(Xb))):
+        for weight in (w, None):
+            for eps in (1e-6, 0.5):
+                Y = o.rmsnorm_rows(src, eps, weight)
+                for r in range(M):
+                    want = rmsnorm_exact(xw[r], eps, weight)
+                    for i in range(K):
+                        assert F(Y[r, i]) == want[i], f"rmsnorm ({r},{i}) eps={eps} w={weight is not None}"
+
+
+def pin_rmsnorm_closed_forms(o):
+    """Constant rows of +-2^k normalize to +-1 exactly (eps = 0), times the
+    weight with one; a zero row stays zero for eps > 0; with eps = 0 the
+    result does not change when the row is scaled by a power of two; a row
+    stride is honoured."""
+    K = 256
+    rows = [np.full(K, s * 2.0 ** k, np.float32) for s in (1, -1) for k in (-20, -3, 0, 7, 30)]
+    X = np.stack(rows)
+    Y = o.rmsnorm_rows(X, 0.0)
+    assert np.array_equal(Y, np.sign(X)), "constant rows"
+    rng = np.random.default_rng(47)
+    w = rng.standard_normal(K).astype(np.float32)
+    assert np.array_equal(o.rmsnorm_rows(X, 0.0, w), np.sign(X) * w), "constant rows, weight"
+    assert np.array_equal(o.rmsnorm_rows(np.zeros((2, K), np.float32), 1e-5), np.zeros((2, K))), "zero row"
+    R = workloads.gaussian_activations(rng, 4, K, 0.01, 20.0, workloads.F32)
+    base = o.rmsnorm_rows(R, 0.0, w)
+    for k in (-9, 5, 21):
+        assert np.array_equal(o.rmsnorm_rows((R * 2.0 ** k).astype(np.float32), 0.0, w), base), f"2^{k}"
+    wide = workloads.gaussian_activations(rng, 3, K + 64, 0.01, 20.0, workloads.F32)
+    assert np.array_equal(o.rmsnorm_rows(wide, 1e-6, w, K=K),
+                          o.rmsnorm_rows(np.ascontiguousarray(wide[:, :K]), 1e-6, w))
+
+
+def pin_rmsnorm_fp64_bound(o):
+    """Against x / sqrt(mean(x^2) + eps) * w in binary64: within the error bound
+    of the binary32 steps (block sums (6 + K/64) roundings, halved by the root,
+    plus 6 more), for eps well below and well above the mean square."""
+    rng = np.random.default_rng(48)
+    for K in (64, 1024, 3072):
+        X = workloads.gaussian_activations(rng, 3, K, 0.005, 30.0, workloads.F32)
+        w = (1.0 + rng.standard_normal(K) * 0.2).astype(np.float32)
+        x64 = X.astype(np.float64)
+        for eps in (1e-6, 4.0 * float(np.mean(x64 ** 2))):
+            ref = x64 / np.sqrt(np.mean(x64 ** 2, axis=1, keepdims=True) + float(np.float32(eps))) * w
+            got = o.rmsnorm_rows(X, eps, w).astype(np.float64)
+            bound = ((6 + K / 64) / 2 + 6) * U32 * np.abs(ref) + 1e-30
+            assert np.all(np.abs(got - ref) <= bound), f"K={K} eps={eps}: {np.max(np.abs(got - ref) / bound)}"
+
+
 def load_int4_golden():
     rows = []
     with open(os.path.join(GOLDEN, "int4_bytes.txt")) as f:

@@ -63,6 +63,12 @@ MUTATIONS = {
     "gate_row_index": ("t = t * gate[o];", "t = t * gate[r % N];"),
     "zero_row_scale": ("        *s_out = 0.0f;\n        memset(q, 0, (size_t)K);\n        return;",
                        "        m = 1.0f;"),
+    "rms_sum_not_mean": ("const float mean = S / (float)K;", "const float mean = S;"),
+    "rms_eps_after_root": ("const float d = sqrtf(mean + eps);", "const float d = sqrtf(mean) + eps;"),
+    "rms_no_reciprocal": ("const float rs = 1.0f / d;", "const float rs = d;"),
+    "rms_abs_not_square": ("sq[i] = x * x;", "sq[i] = fabsf(x);"),
+    "rms_weight_reversed": ("y = y * weight[i];", "y = y * weight[K - 1 - i];"),
+    "rms_last_block_only": ("S = b == 0 ? block : S + block;", "S = block;"),
 }
 
 
