@@ -58,11 +58,12 @@ def source_hash(path: str) -> str:
 
 
 def quantize_bytes(w: workloads.Workload) -> int:
-    """Algorithmic bytes of one quantize pass: read X once (and the Modulate
-    producer's two per-channel vectors, if any), write the packed tensor."""
+    """Algorithmic bytes of one quantize pass: read X once (and the producer's
+    per-channel vectors, if any: RMSNorm weight, Modulate scale and shift),
+    write the packed tensor."""
     esz = 2 if w.x_dtype == workloads.BF16 else 4
     m_pad = (w.M + 3) // 4 * 4
-    mod = 8 * w.K if w.modulate else 0
+    mod = (8 * w.K if w.modulate else 0) + (4 * w.K if w.rmsnorm else 0)
     return w.M * w.K * esz + m_pad * w.K + 4 * m_pad + mod
 
 
@@ -161,6 +162,8 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
     X = np.ascontiguousarray(inp.X[:rows])
     t0 = time.perf_counter()
+    if w.rmsnorm:
+        X = o.rmsnorm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
     if w.modulate:
         X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
     if w.gated:
@@ -172,7 +175,8 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     dt = time.perf_counter() - t0
     ops = 2 * rows * w.N * w.K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.M} rows of {w.name} ({'modulate + ' if w.modulate else ''}"
+            "sample": f"{rows} of {w.M} rows of {w.name} ({'RMSNorm + ' if w.rmsnorm else ''}"
+                      f"{'modulate + ' if w.modulate else ''}"
                       f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''} "
                       f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
 
@@ -258,6 +262,9 @@ def main() -> int:
 
     mod = (cr.Modulate(torch.from_numpy(inp.mod_scale).to(dev), torch.from_numpy(inp.mod_shift).to(dev))
            if w.modulate else None)
+    if w.rmsnorm:
+        mod = cr.RMSNormModulate(w.rms_eps, torch.from_numpy(inp.norm_weight).to(dev),
+                                 mod.scale if mod else None, mod.shift if mod else None)
 
     def quantize(i):
         Xd, ws, Ys = sets[i % n_sets]
@@ -344,6 +351,7 @@ def main() -> int:
         "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W {'i4' if w.w_bits == 4 else 'i8'} [{w.N},{w.K}] x "
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
                                f"{list(w.input_scales)}"
+                               + (", RMSNorm -> Mul(weight) fused" if w.rmsnorm else "")
                                + (", Modulate producer fused" if w.modulate else "")
                                + (", gated residual in place" if w.gated else ""),
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,

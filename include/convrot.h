@@ -168,28 +168,49 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
  *     x' = (x + x * scale[i]) + shift[i]       i = input feature (column)
  * three separately rounded binary32 operations; shift may be NULL (scale-only
  * modulation, no add).  scale and shift are device vectors of K floats shared
- * by every row, 16-byte aligned. */
-typedef enum { CONVROT_PRE_NONE = 0, CONVROT_PRE_MODULATE = 1 } convrot_pre_kind;
+ * by every row, 16-byte aligned.
+ *
+ * CONVROT_PRE_RMSNORM_MODULATE (same page and section: the RMSNorm ->
+ * Mul(weight) -> Mul(modulation) -> Add -> Add(shift) -> ConvRot fusion) puts
+ * RMSNorm -> Mul(weight) ahead of the Modulate above.  The page does not
+ * spell out RMSNorm's arithmetic; per row, with x the widened input:
+ *     S = sum of fl(x * x): pairwise within each block of 64 consecutive
+ *         features (adjacent pairs, then pairs of those sums, ...), then the
+ *         K/64 block sums added left to right
+ *     r = fl(1 / fl(sqrt(fl(fl(S / K) + eps))))     (correctly rounded)
+ *     x' = fl(x * r), then fl(x' * norm_weight[i]) when norm_weight is given
+ * and then Modulate with scale and shift, which are both optional here (no
+ * scale: no modulation; shift requires scale).  eps is finite and >= 0;
+ * inputs whose squares or sums overflow binary32 are outside the contract.
+ * Rows are limited to half the quantizer's K (32768 when K % 256 == 0), else
+ * CONVROT_EUNSUPPORTED. */
+typedef enum {
+    CONVROT_PRE_NONE = 0,
+    CONVROT_PRE_MODULATE = 1,
+    CONVROT_PRE_RMSNORM_MODULATE = 2
+} convrot_pre_kind;
 
 typedef struct {
-    int kind;             /* convrot_pre_kind */
-    const float *scale;   /* MODULATE: [K] (device), required */
-    const float *shift;   /* MODULATE: [K] (device) or NULL */
+    int kind;                  /* convrot_pre_kind */
+    const float *scale;        /* MODULATE: [K] (device), required; RMSNORM_MODULATE: [K] or NULL */
+    const float *shift;        /* [K] (device) or NULL */
+    const float *norm_weight;  /* RMSNORM_MODULATE: [K] (device) or NULL */
+    float eps;                 /* RMSNORM_MODULATE: added to the mean square */
 } convrot_pre;
 
 /* convrot_quantize_rows with a producer.  pre may be NULL or of kind
  * CONVROT_PRE_NONE (then identical to convrot_quantize_rows).  CONVROT_EINVAL
- * for a MODULATE descriptor without scale or with misaligned vectors,
- * CONVROT_EUNSUPPORTED for an unknown kind, CONVROT_EOVERLAP if packed
- * overlaps X, scale or shift. */
+ * for a MODULATE descriptor without scale, a shift without scale, a negative
+ * or non-finite eps, or misaligned vectors (16 bytes); CONVROT_EUNSUPPORTED
+ * for an unknown kind; CONVROT_EOVERLAP if packed overlaps X or a vector. */
 int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                               const convrot_pre *pre, int group_size, float input_scale,
                               void *packed, void *stream);
 
 /* convrot_int8_linear_shared with a producer applied in every quantization
- * pass (same rules for pre as above).  The workspace must not overlap scale or
- * shift; an output may alias them (they are consumed before any output is
- * written), like X. */
+ * pass (same rules for pre as above).  The workspace must not overlap the
+ * producer's vectors; an output may alias them (they are consumed before any
+ * output is written), like X. */
 int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                    const convrot_pre *pre, int group_size, int n,
                                    const convrot_linear_desc *descs, void *workspace,

@@ -16,7 +16,7 @@ LIBRARY = os.path.join(_HERE, "libconvrot.so")
 
 OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
-PRE_NONE, PRE_MODULATE = 0, 1
+PRE_NONE, PRE_MODULATE, PRE_RMSNORM_MODULATE = 0, 1, 2
 POST_NONE, POST_GATED_RESIDUAL = 0, 1
 MAX_LINEARS = 16
 
@@ -49,6 +49,8 @@ class PreDesc(ctypes.Structure):
         ("kind", ctypes.c_int),
         ("scale", ctypes.c_void_p),
         ("shift", ctypes.c_void_p),
+        ("norm_weight", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
     ]
 
 
@@ -62,7 +64,22 @@ class Modulate:
 
     def desc(self) -> PreDesc:
         return PreDesc(PRE_MODULATE, self.scale.data_ptr(),
-                       None if self.shift is None else self.shift.data_ptr())
+                       None if self.shift is None else self.shift.data_ptr(), None, 0.0)
+
+
+class RMSNormModulate:
+    """RMSNorm -> Mul(weight) -> Modulate ahead of the quantizer: eps, and
+    float32 device vectors of K elements, each optional (weight None: no
+    weight multiplication; scale None: no modulation; shift needs scale)."""
+
+    def __init__(self, eps: float, weight=None, scale=None, shift=None):
+        self.eps = float(eps)
+        self.weight, self.scale, self.shift = weight, scale, shift
+
+    def desc(self) -> PreDesc:
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return PreDesc(PRE_RMSNORM_MODULATE, ptr(self.scale), ptr(self.shift), ptr(self.weight),
+                       self.eps)
 
 
 class PostDesc(ctypes.Structure):

@@ -153,22 +153,38 @@ GemmLinear make_linear(const int8_t *Qw, const float *s_w, const float *bias, in
 int out_kind_of(int y_dtype) { return y_dtype == CONVROT_BF16 ? kOutBF16 : kOutF32; }
 
 // Validates a producer descriptor (nullable) and returns the spans it reads.
-int check_pre(const convrot_pre *pre, int64_t K, PreOp *op, Span *s_scale, Span *s_shift)
+// The producer's device vectors, for overlap checks.
+struct PreSpans {
+    Span scale, shift, weight;
+    bool hits(const Span &s) const { return overlap(scale, s) || overlap(shift, s) || overlap(weight, s); }
+};
+
+int check_pre(const convrot_pre *pre, int64_t K, PreOp *op, PreSpans *spans)
 {
     *op = PreOp{};
-    *s_scale = Span{};
-    *s_shift = Span{};
+    *spans = PreSpans{};
     if (!pre || pre->kind == CONVROT_PRE_NONE)
         return CONVROT_OK;
-    if (pre->kind != CONVROT_PRE_MODULATE)
+    if (pre->kind != CONVROT_PRE_MODULATE && pre->kind != CONVROT_PRE_RMSNORM_MODULATE)
         return CONVROT_EUNSUPPORTED;
-    if (!pre->scale || !aligned(pre->scale, 16) || (pre->shift && !aligned(pre->shift, 16)))
+    const bool rms = pre->kind == CONVROT_PRE_RMSNORM_MODULATE;
+    if ((!rms && !pre->scale) || (pre->shift && !pre->scale))
         return CONVROT_EINVAL;
-    op->kind = kPreModulate;
+    if ((pre->scale && !aligned(pre->scale, 16)) || (pre->shift && !aligned(pre->shift, 16)))
+        return CONVROT_EINVAL;
+    if (rms && ((pre->norm_weight && !aligned(pre->norm_weight, 16)) || !std::isfinite(pre->eps) ||
+                pre->eps < 0.0f))
+        return CONVROT_EINVAL;
+    if (rms && K > quantize_max_k(K, true))
+        return CONVROT_EUNSUPPORTED;
+    op->kind = rms ? kPreRmsNormModulate : kPreModulate;
     op->scale = pre->scale;
     op->shift = pre->shift;
-    *s_scale = span_of(pre->scale, 4 * K);
-    *s_shift = span_of(pre->shift, 4 * K);
+    op->norm_weight = rms ? pre->norm_weight : nullptr;
+    op->eps = rms ? pre->eps : 0.0f;
+    spans->scale = span_of(pre->scale, 4 * K);
+    spans->shift = span_of(pre->shift, 4 * K);
+    spans->weight = span_of(op->norm_weight, 4 * K);
     return CONVROT_OK;
 }
 
@@ -199,8 +215,8 @@ int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, 
     if (rc != CONVROT_OK)
         return rc;
     PreOp op;
-    Span sc, sh;
-    rc = check_pre(pre, K, &op, &sc, &sh);
+    PreSpans ps;
+    rc = check_pre(pre, K, &op, &ps);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0)
@@ -208,8 +224,7 @@ int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, 
     if (!packed || !aligned(packed, 16))
         return CONVROT_EINVAL;
     const Span out = span_of(packed, (int64_t)convrot_packed_bytes(M, K));
-    if (overlap(rows_span(X, M, K, ldx, elem_bytes(x_dtype)), out) || overlap(sc, out) ||
-        overlap(sh, out))
+    if (overlap(rows_span(X, M, K, ldx, elem_bytes(x_dtype)), out) || ps.hits(out))
         return CONVROT_EOVERLAP;
     (void)hipGetLastError();
     return hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, input_scale, op, packed,
@@ -399,8 +414,8 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
     if (rc != CONVROT_OK)
         return rc;
     PreOp op;
-    Span sc, sh;
-    rc = check_pre(pre, K, &op, &sc, &sh);
+    PreSpans ps;
+    rc = check_pre(pre, K, &op, &ps);
     if (rc != CONVROT_OK)
         return rc;
     rc = check_contraction_k(K);
@@ -436,7 +451,7 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
         return CONVROT_EINVAL;
     const Span ws = span_of(workspace, slot_bytes * n_slots);
     const Span xs = rows_span(X, M, K, ldx, elem_bytes(x_dtype));
-    if (overlap(ws, xs) || overlap(ws, sc) || overlap(ws, sh))
+    if (overlap(ws, xs) || ps.hits(ws))
         return CONVROT_EOVERLAP;
     for (int i = 0; i < n; ++i) {
         if (overlap(chk[i].y, ws) || overlap(chk[i].qw, ws) || overlap(chk[i].sw, ws) ||

@@ -9,16 +9,19 @@ namespace convrot_detail {
 
 // ---------------------------------------------------------------- quantize
 // Largest row (in elements) the quantizer handles for a given K: one
-// workgroup per group of rows, at most 256 quads of 4 lanes per row.
-int64_t quantize_max_k(int64_t K);
+// workgroup per group of rows, at most 256 quads of 4 lanes per row (128 with
+// the RMSNorm producer).
+int64_t quantize_max_k(int64_t K, bool rmsnorm = false);
 
 // Producer applied to each widened input element before the rotation.
-enum PreKind : int { kPreNone = 0, kPreModulate = 1 };
+enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2 };
 
 struct PreOp {
     int kind = kPreNone;
-    const float *scale = nullptr;   // kPreModulate: per-channel [K], 16-byte aligned
-    const float *shift = nullptr;   // kPreModulate: per-channel [K] or null
+    const float *scale = nullptr;         // per-channel [K] or null (no modulation), 16-byte aligned
+    const float *shift = nullptr;         // per-channel [K] or null (needs scale)
+    const float *norm_weight = nullptr;   // kPreRmsNormModulate: per-channel [K] or null
+    float eps = 0.0f;                     // kPreRmsNormModulate
 };
 
 // Launch the (producer +) rotate + row-max + quantize + pack kernel.

@@ -7,6 +7,9 @@
 //                                           "ggml operator extensions", section
 //                                           "sd.cpp integration"; per-channel
 //                                           vectors, shift optional)
+//   x  = fl(x * r) [* w]                   (optional RMSNorm -> Mul(weight)
+//                                           ahead of Modulate, same page and
+//                                           section; r per row, see below)
 //   x  = x * alpha                         (multiply only when alpha != 1)
 //   y  = x R_G per contiguous G-group       (R_G = H4^(x)n, G = 4^n)
 //   m  = max |y| over the whole row
@@ -179,6 +182,74 @@ __device__ __forceinline__ float quad_abs_max(const float (&v)[NC][8])
     return fmaxf(m, quad_swap<kQuadPermXor2>(m));
 }
 
+// Correctly rounded binary32 square root of a finite x >= 0.  Start from the
+// hardware's approximation and step to the neighbour while sqrt(x) lies
+// outside the candidate's rounding interval; the interval ends have at most
+// 25 significant bits, so their squares compare with x exactly in binary64
+// (a tie at an end goes to the even candidate).
+__device__ __forceinline__ float sqrt_rn(float x)
+{
+    if (!(x > 0.0f) || x == __builtin_huge_valf())
+        return x;
+    float s = __builtin_sqrtf(x);
+    const double xd = x;
+    for (int it = 0; it < 4; ++it) {
+        const unsigned b = __builtin_bit_cast(unsigned, s);
+        const float below = __builtin_bit_cast(float, b - 1u);
+        const float above = __builtin_bit_cast(float, b + 1u);
+        const double lo = 0.5 * ((double)s + (double)below);
+        const double hi = 0.5 * ((double)s + (double)above);
+        const bool odd = (b & 1u) != 0;
+        if (lo * lo > xd || (lo * lo == xd && odd))
+            s = below;
+        else if (hi * hi < xd || (hi * hi == xd && odd))
+            s = above;
+        else
+            break;
+    }
+    return s;
+}
+
+// RMSNorm's sums of squares for the quad's 64-feature blocks (block b = chunks
+// 2b and 2b+1): the pairwise tree of the 64 squares, adjacent pairs first.
+// Its levels are the element index bits: 0..2 in the chunk, 3 = lane bit 0,
+// 4 = chunk bit 0, 5 = lane bit 1; IEEE addition being commutative, both
+// lanes of a DPP pair hold the same bits.  Every lane of the quad ends with
+// every block sum.
+template <int NC>
+__device__ __forceinline__ void block_sums_sq(const float (&v)[NC][8], float (&bs)[NC / 2])
+{
+#pragma unroll
+    for (int b = 0; b < NC / 2; ++b) {
+        float s16[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float(&x)[8] = v[2 * b + h];
+            float q[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                q[p] = x[p] * x[p];
+            const float a0 = q[0] + q[1], a1 = q[2] + q[3], a2 = q[4] + q[5], a3 = q[6] + q[7];
+            const float s8 = (a0 + a1) + (a2 + a3);
+            s16[h] = s8 + quad_swap<kQuadPermXor1>(s8);
+        }
+        const float s32 = s16[0] + s16[1];
+        bs[b] = s32 + quad_swap<kQuadPermXor2>(s32);
+    }
+}
+
+// x = fl(x * w[col + p]) on one chunk (RMSNorm's weight), read through the
+// caches like the Modulate vectors.
+__device__ __forceinline__ void weight8(float (&v)[8], const float *__restrict__ w, int64_t col)
+{
+    const v4f w0 = *reinterpret_cast<const v4f *>(w + col);
+    const v4f w1 = *reinterpret_cast<const v4f *>(w + col + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+        v[p] = v[p] * wv[p];
+}
+
 // Codes of one chunk: rne(fl(y * inv)) in two's complement, 8 bytes.
 __device__ __forceinline__ v2u encode8(const float (&v)[8], float inv)
 {
@@ -238,21 +309,34 @@ __device__ __forceinline__ void modulate8(float (&v)[8], const float *__restrict
     }
 }
 
-template <typename XT, int G, int NC, bool SCALED, int MOD>
-__global__ __launch_bounds__(1024) void quantize_rows_kernel(
+//
+// RMSNorm (RMS = true) takes two more workgroup phases before the Modulate:
+// each quad stores its 64-feature block sums of squares in LDS; one lane per
+// row adds the row's K/64 block sums left to right and forms
+// r = fl(1 / fl(sqrt(fl(fl(S / K) + eps)))) with correctly rounded operations;
+// every lane then scales its values by its row's r (and the weight).
+//
+// With RMSNorm the workgroup has at most 512 threads (two waves per SIMD), so
+// that the row data, the block sums and the vectors fit in registers.
+template <typename XT, int G, int NC, bool SCALED, int MOD, bool RMS>
+__global__ __launch_bounds__(RMS ? 512 : 1024) void quantize_rows_kernel(
     const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
     const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
+    const float *__restrict__ norm_weight, float eps,
     int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
     static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    constexpr int kBlocks = NC / 2;                      // 64-feature blocks per quad span
     __shared__ unsigned row_max[256];
+    __shared__ float norm_part[RMS ? 256 * kBlocks : 1];
+    __shared__ float norm_r[RMS ? 256 : 1];
 
     const int tid = threadIdx.x;
     const int quad = tid >> 2;
     const int j0 = tid & 1, j1 = (tid >> 1) & 1;
     int row_local, q_in_row;
-    quad_place<MOD>(quad, quads_per_row, rows_per_wg, row_local, q_in_row);
+    quad_place<(MOD != 0 || RMS) ? 1 : 0>(quad, quads_per_row, rows_per_wg, row_local, q_in_row);
     const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
     const int64_t span0 = (int64_t)q_in_row * (32 * NC);
     // A quad never straddles rows, so this branch is uniform per quad and the
@@ -269,6 +353,42 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             load8(xr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1), v[c]);
+    }
+    if constexpr (RMS) {
+        const int row_blocks = quads_per_row * kBlocks;
+        if (live) {
+            float bs[kBlocks];
+            block_sums_sq<NC>(v, bs);
+            if ((tid & 3) == 0)
+#pragma unroll
+                for (int b = 0; b < kBlocks; ++b)
+                    norm_part[row_local * row_blocks + q_in_row * kBlocks + b] = bs[b];
+        }
+        __syncthreads();
+        if (tid < rows_per_wg) {
+            const float *bp = norm_part + tid * row_blocks;
+            float sum = bp[0];
+            for (int b = 1; b < row_blocks; ++b)
+                sum = sum + bp[b];
+            const float mean = __fdiv_rn(sum, (float)K);
+            norm_r[tid] = __fdiv_rn(1.0f, sqrt_rn(mean + eps));
+        }
+        __syncthreads();
+        if (live) {
+            const float r = norm_r[row_local];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    v[c][p] = v[c][p] * r;
+            if (norm_weight) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    weight8(v[c], norm_weight, span0 + chunk_offset(j0, j1, c));
+            }
+        }
+    }
+    if (live) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             modulate8<MOD>(v[c], mod_scale, mod_shift, span0 + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1));
@@ -487,87 +607,100 @@ int gcd_int(int a, int b)
     return a;
 }
 
-template <typename XT, int G, int NC, int MOD>
+template <typename XT, int G, int NC, int MOD, bool RMS>
 void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                   void *packed, hipStream_t stream)
 {
     const int64_t m_pad = (M + 3) / 4 * 4;
     const int qr = (int)(K / (32 * NC));
+    constexpr int kMaxThreads = RMS ? 512 : 1024;
     // smallest row count that fills whole waves, then grow towards 256 threads
     int rows = 16 / gcd_int(qr, 16);
-    if (4 * qr * rows > 1024)
-        rows = 1024 / (4 * qr) > 0 ? 1024 / (4 * qr) : 1;
+    if (4 * qr * rows > kMaxThreads)
+        rows = kMaxThreads / (4 * qr) > 0 ? kMaxThreads / (4 * qr) : 1;
     while (4 * qr * rows * 2 <= 256)
         rows *= 2;
     const int threads = 4 * qr * rows;
     const int64_t blocks = (m_pad + rows - 1) / rows;
     int8_t *Q = static_cast<int8_t *>(packed);
     float *S = reinterpret_cast<float *>(Q + m_pad * K);
-    if constexpr (sizeof(XT) == 4) {
+    if constexpr (sizeof(XT) == 4 && !RMS) {
         // binary32 rows of up to 256 threads per workgroup take the staged kernel
         if (threads <= 256)
             return launch_staged<G, NC, MOD>(static_cast<const float *>(X), M, K, ldx, alpha, pre, Q,
                                              S, m_pad, qr, rows, stream);
     }
     if (alpha != 1.0f)
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, pre.scale, pre.shift, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, Q, S, qr, rows);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, RMS>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, pre.scale, pre.shift, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, Q, S, qr, rows);
 }
 
-template <typename XT, int NC, int MOD>
+template <typename XT, int NC, int MOD, bool RMS>
 void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
-    case 4: launch_typed<XT, 4, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 16: launch_typed<XT, 16, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 64: launch_typed<XT, 64, NC, MOD>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 4: launch_typed<XT, 4, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 16: launch_typed<XT, 16, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 64: launch_typed<XT, 64, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
     default:
         if constexpr (NC == 8)
-            launch_typed<XT, 256, 8, MOD>(X, M, K, ldx, alpha, pre, packed, stream);
+            launch_typed<XT, 256, 8, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream);
         break;
     }
 }
 
-template <typename XT, int MOD>
+template <typename XT, int MOD, bool RMS>
 void launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                   const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (K % 256 == 0)
-        launch_nc<XT, 8, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 8, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else if (K % 128 == 0)
-        launch_nc<XT, 4, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 4, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_nc<XT, 2, MOD>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 2, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+}
+
+template <typename XT, bool RMS>
+void launch_mod(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                const PreOp &pre, void *packed, hipStream_t stream)
+{
+    if (pre.scale && pre.shift)
+        launch_dtype<XT, 2, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else if (pre.scale)
+        launch_dtype<XT, 1, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else
+        launch_dtype<XT, 0, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT>
 void launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                 const PreOp &pre, void *packed, hipStream_t stream)
 {
-    if (pre.kind == kPreModulate && pre.shift)
-        launch_dtype<XT, 2>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else if (pre.kind == kPreModulate)
-        launch_dtype<XT, 1>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (pre.kind == kPreRmsNormModulate)
+        launch_mod<XT, true>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_dtype<XT, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_mod<XT, false>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 }  // namespace
 
-int64_t quantize_max_k(int64_t K)
+int64_t quantize_max_k(int64_t K, bool rmsnorm)
 {
-    // 256 quads per row at most; a quad covers 256, 128 or 64 elements.
+    // 256 quads per row at most (128 with RMSNorm); a quad covers 256, 128
+    // or 64 elements.
+    const int64_t quads = rmsnorm ? 128 : 256;
     if (K % 256 == 0)
-        return 256 * 256;
+        return quads * 256;
     if (K % 128 == 0)
-        return 256 * 128;
-    return 256 * 64;
+        return quads * 128;
+    return quads * 64;
 }
 
 hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,

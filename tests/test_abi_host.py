@@ -97,8 +97,8 @@ def test_quantize_validation(lib):
 
 
 def qpre(lib, kind=cr.PRE_MODULATE, sc=BASE + 96 * MB, sh=BASE + 97 * MB, M=8, K=256,
-         packed=BASE + 64 * MB, raw=False):
-    d = None if raw else ctypes.byref(cr.PreDesc(kind, sc, sh))
+         packed=BASE + 64 * MB, raw=False, w=None, eps=0.0):
+    d = None if raw else ctypes.byref(cr.PreDesc(kind, sc, sh, w, eps))
     return lib.convrot_quantize_rows_pre(ctypes.c_void_p(BASE), cr.F32, M, K, K, d, 16,
                                          ctypes.c_float(1.0), ctypes.c_void_p(packed), None)
 
@@ -113,8 +113,26 @@ def test_producer_validation(lib):
     assert qpre(lib, M=0) == OK
     assert qpre(lib, M=0, raw=True) == OK                # NULL producer
     assert qpre(lib, kind=cr.PRE_NONE, sc=0, sh=0, M=0) == OK
+    # RMSNorm -> Mul(weight) -> Modulate: scale optional, shift needs it,
+    # eps finite and >= 0, aligned weight that packed does not overlap, rows
+    # up to half the quantizer's K
+    rms = cr.PRE_RMSNORM_MODULATE
+    w = BASE + 98 * MB
+    assert qpre(lib, kind=rms, w=w, eps=1e-6, M=0) == OK
+    assert qpre(lib, kind=rms, sc=0, sh=0, w=0, eps=0.0, M=0) == OK     # plain RMSNorm
+    assert qpre(lib, kind=rms, sc=0, w=w) == EINVAL                     # shift without scale
+    assert qpre(lib, kind=rms, w=w, eps=-1e-6) == EINVAL
+    assert qpre(lib, kind=rms, w=w, eps=float("inf")) == EINVAL
+    assert qpre(lib, kind=rms, w=w, eps=float("nan")) == EINVAL
+    assert qpre(lib, kind=rms, w=w + 8) == EINVAL
+    assert qpre(lib, kind=rms, w=BASE + 64 * MB + 1024) == EOVL        # packed overlaps the weight
+    assert qpre(lib, kind=rms, w=w, K=32768 + 256) == EUNSUP
     # the shared entry: the workspace must not overlap the vectors
     d = cr.LinearDesc(BASE + 16 * MB, None, None, 32, 1.0, BASE + 32 * MB, cr.F32, 32)
+    pre = cr.PreDesc(cr.PRE_RMSNORM_MODULATE, None, None, BASE + 48 * MB + 512, 1e-6)
+    f = lib.convrot_int8_linear_shared_pre
+    assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),
+             ctypes.c_void_p(BASE + 48 * MB), MB, None) == EOVL
     pre = cr.PreDesc(cr.PRE_MODULATE, BASE + 48 * MB + 256, None)
     f = lib.convrot_int8_linear_shared_pre
     assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),

@@ -28,6 +28,8 @@ Recipe, per workload (fixed draw order):
     when the workload has a gated-residual epilogue:
         gate = rng.standard_normal(N, float32) * 0.3
         residual = rng.standard_normal((M, N), float32), in the output dtype
+    when the workload has an RMSNorm -> Mul(weight) producer (eps 1e-6):
+        norm_weight = 1 + rng.standard_normal(K, float32) * 0.1
     when the workload has a Modulate producer (per-channel vectors, as the
     adaLN modulation of a DiT block supplies them):
         scale = rng.standard_normal(K, float32) * 0.3
@@ -59,6 +61,8 @@ class Workload:
     modulate: bool = False            # a Modulate producer before the rotation
     w_bits: int = 8                   # 4: convrot_w4a4 packed weights
     gated: bool = False               # a gated-residual epilogue after the linear
+    rmsnorm: bool = False             # RMSNorm -> Mul(weight) ahead of the Modulate
+    rms_eps: float = 1e-6
     note: str = ""
 
     @property
@@ -79,6 +83,9 @@ WORKLOADS = {
     "mlp_up_mod": Workload("mlp_up_mod", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=5,
                            modulate=True,
                            note="DiT MLP up-projection with its Modulate producer fused"),
+    "mlp_up_rms": Workload("mlp_up_rms", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=8,
+                           modulate=True, rmsnorm=True,
+                           note="DiT MLP up-projection with RMSNorm -> Mul(weight) -> Modulate fused"),
     "mlp_up_w4": Workload("mlp_up_w4", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=6,
                           w_bits=4, note="DiT MLP up-projection with convrot_w4a4 weights"),
     "proj_gated": Workload("proj_gated", 4096, 3072, 3072, 256, BF16, BF16, (1.0,), seed=7,
@@ -132,6 +139,7 @@ class Inputs:
     W: list = field(default_factory=list)   # float32 [N,K] per linear
     b: list = field(default_factory=list)   # float32 [N] per linear
     s_w: list = field(default_factory=list) # float32 [N] per linear (4-bit weights only)
+    norm_weight: np.ndarray | None = None   # float32 [K] (RMSNorm producer)
     mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
     mod_shift: np.ndarray | None = None     # float32 [K]
     gate: np.ndarray | None = None          # float32 [N] (gated residual)
@@ -156,12 +164,19 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
         W, b = gaussian_weights(rng, w.N, w.K)
         inp.W.append(W)
         inp.b.append(b)
+    if w.rmsnorm:
+        inp.norm_weight = norm_weight(rng, w.K)
     if w.modulate:
         inp.mod_scale, inp.mod_shift = modulation(rng, w.K)
     if w.gated:
         inp.gate = rng.standard_normal(w.N, dtype=np.float32) * np.float32(0.3)
         inp.residual = gaussian_activations(rng, rows, w.N, 0.0, 1.0, w.y_dtype)
     return inp
+
+
+def norm_weight(rng: np.random.Generator, K: int, sigma: float = 0.1):
+    """RMSNorm weight 1 + N(0, sigma), fp32 [K]."""
+    return np.float32(1.0) + rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
 
 
 def modulation(rng: np.random.Generator, K: int, sigma: float = 0.3):
