@@ -81,6 +81,9 @@ class Packed:
         return self.s_all[: self.M]
 
 
+ACT_SILU, ACT_SIGMOID = 1, 2
+
+
 class Oracle:
     """ctypes wrapper over a built oracle shared library."""
 
@@ -98,6 +101,8 @@ class Oracle:
             "oracle_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i32]),
             "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
             "oracle_rmsnorm_rows": (i32, [vp, i32, i64, i64, i64, f32, vp, vp, i32]),
+            "oracle_expf": (f32, [f32]),
+            "oracle_gated_act_rows": (i32, [vp, i32, i64, i64, i64, vp, i64, i32, vp, i32]),
             "oracle_unpack_int4": (i32, [vp, i64, i64, vp]),
             "oracle_gated_residual": (i32, [vp, i64, i64, f32, vp, vp, i32, i64, i32, vp, i64, i32]),
             "oracle_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, i32]),
@@ -176,6 +181,27 @@ class Oracle:
         rc = self.lib.oracle_rmsnorm_rows(_p(X), code, M, K, ldx, ctypes.c_float(eps),
                                           None if w is None else _p(w), _p(Y), threads)
         self._check(rc, "rmsnorm_rows")
+        return Y
+
+    def expf(self, x: float) -> float:
+        """exp rounded once to binary32 (the oracle's exp)."""
+        return float(self.lib.oracle_expf(ctypes.c_float(x)))
+
+    def gated_act_rows(self, X: np.ndarray, U: np.ndarray, act: int, K: int | None = None,
+                       threads: int = 1) -> np.ndarray:
+        """fl(act(X) * U) on the first K columns (act: ACT_SILU or ACT_SIGMOID);
+        X and U share their dtype.  Returns binary32 [M, K]."""
+        code = _dtype_code(X)
+        assert _dtype_code(U) == code
+        X = np.ascontiguousarray(X)
+        U = np.ascontiguousarray(U)
+        M, ldx = X.shape
+        K = ldx if K is None else K
+        assert U.shape[0] == M and U.shape[1] >= K
+        Y = np.empty((M, K), dtype=np.float32)
+        rc = self.lib.oracle_gated_act_rows(_p(X), code, M, K, ldx, _p(U), U.shape[1], act, _p(Y),
+                                            threads)
+        self._check(rc, "gated_act_rows")
         return Y
 
     def unpack_int4(self, W4: np.ndarray, K: int) -> np.ndarray:

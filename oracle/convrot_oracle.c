@@ -55,6 +55,16 @@
  *     those sums, ...) and the K/64 block sums are added left to right; then
  *     mean = fl(S / K), d = fl(sqrt(fl(mean + eps))), r = fl(1 / d) (each
  *     correctly rounded), y = fl(x * r) and, with a weight, fl(y * w[i]).
+ *   - the gated activation ahead of the quantizer (same page and section:
+ *     SiLU/Sigmoid -> Mul -> ConvRot, and SwiGLU -> ConvRot with its gate and
+ *     up halves): z = fl(act(g) * u) with g the quantizer's input and u a
+ *     second tensor of the same shape; sigmoid(g) = fl(1 / fl(1 + e)) with
+ *     e = exp(-g) correctly rounded to binary32, and silu(g) =
+ *     fl(g * sigmoid(g)).  exp is evaluated in x87 extended precision
+ *     (64-bit significand, error a few units in 2^-64) and rounded once to
+ *     binary32: the binary32 arguments whose exp lies closest to a binary32
+ *     rounding boundary are still far above that error, so the result is the
+ *     correctly rounded exp.
  */
 #include <math.h>
 #include <stdint.h>
@@ -336,6 +346,48 @@ int oracle_rmsnorm_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_
             if (weight)
                 y = y * weight[i];
             Y[r * K + i] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * exp(x) rounded once to binary32 from x87 extended precision (the reading
+ * stated at the top of this file).
+ */
+float oracle_expf(float x)
+{
+    return (float)expl((long double)x);
+}
+
+#define ORACLE_ACT_SILU 1
+#define ORACLE_ACT_SIGMOID 2
+
+/*
+ * The gated activation (page "ggml operator extensions", section "sd.cpp
+ * integration": SiLU/Sigmoid -> Mul -> ConvRot and SwiGLU -> ConvRot), in the
+ * reading stated at the top of this file: Y[r, i] = fl(act(g) * u) with
+ * g = widen(X[r, i]) and u = widen(U[r, i]) (both of dtype x_dtype, row
+ * strides ldx and ldu).  Y is binary32 [M][K], contiguous.
+ */
+int oracle_gated_act_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          const void *U, int64_t ldu, int act, float *Y, int threads)
+{
+    if (!X || !U || !Y || M < 0 || K < 1 || ldx < K || ldu < K)
+        return ORACLE_EINVAL;
+    if ((x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16) ||
+        (act != ORACLE_ACT_SILU && act != ORACLE_ACT_SIGMOID))
+        return ORACLE_EUNSUPPORTED;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t r = 0; r < M; ++r) {
+        for (int64_t i = 0; i < K; ++i) {
+            const float g = load_widened(X, x_dtype, r * ldx + i);
+            const float u = load_widened(U, x_dtype, r * ldu + i);
+            const float e = oracle_expf(-g);
+            const float d = 1.0f + e;
+            const float sg = 1.0f / d;
+            const float a = act == ORACLE_ACT_SILU ? g * sg : sg;
+            Y[r * K + i] = a * u;
         }
     }
     return ORACLE_OK;

@@ -84,6 +84,12 @@ def F(x) -> Fraction:
     return Fraction(float(x))
 
 
+def F_out(x) -> Fraction:
+    """An oracle output as an exact rational; a non-finite one fails the pin."""
+    assert np.isfinite(x), f"non-finite output {x}"
+    return Fraction(float(x))
+
+
 # ----------------------------------------------------------------- the pins
 
 def pin_h4_entries(o):
@@ -478,7 +484,7 @@ def pin_rmsnorm_exact(o):
                 for r in range(M):
                     want = rmsnorm_exact(xw[r], eps, weight)
                     for i in range(K):
-                        assert F(Y[r, i]) == want[i], f"rmsnorm ({r},{i}) eps={eps} w={weight is not None}"
+                        assert F_out(Y[r, i]) == want[i], f"rmsnorm ({r},{i}) eps={eps} w={weight is not None}"
 
 
 def pin_rmsnorm_closed_forms(o):
@@ -518,6 +524,96 @@ def pin_rmsnorm_fp64_bound(o):
             got = o.rmsnorm_rows(X, eps, w).astype(np.float64)
             bound = ((6 + K / 64) / 2 + 6) * U32 * np.abs(ref) + 1e-30
             assert np.all(np.abs(got - ref) <= bound), f"K={K} eps={eps}: {np.max(np.abs(got - ref) / bound)}"
+
+
+def exp_exact_f32(x: float) -> Fraction:
+    """exp(x) to 60 significant digits (Python's decimal), then rounded to
+    binary32 by the IEEE rule above: the correctly rounded binary32 exp."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 60
+        return rne_f32(Fraction(Decimal(float(x)).exp()))
+
+
+def expf_sample(rng, n):
+    """Binary32 arguments over exp's finite range: random bit patterns inside
+    [-103.9, 88.7], plus the ends, zeros, tiny values and small integers."""
+    u = rng.integers(0, 2 ** 32, size=8 * n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    u = u[np.isfinite(u) & (u > -103.9) & (u < 88.7)][:n]
+    special = np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -30, -(2.0 ** -30), 88.72, -103.9, 0.5,
+                        -0.5, 10.0, -10.0, 17.0, -17.0, 1e-7, 87.0, -87.0], np.float32)
+    return np.concatenate([special, u]).astype(np.float32)
+
+
+def pin_expf_correctly_rounded(o):
+    """The oracle's exp equals the correctly rounded binary32 exp (decimal at
+    60 digits) on random arguments over the whole finite range."""
+    rng = np.random.default_rng(71)
+    for x in expf_sample(rng, 6000):
+        got = np.float32(o.expf(float(x)))
+        want = exp_exact_f32(float(x))
+        assert F_out(got) == want, f"exp({float(x)!r}) = {float(got)!r}, want {float(want)!r}"
+
+
+def gated_exact(g: float, u: float, act: int) -> Fraction:
+    e = exp_exact_f32(-float(g))
+    sg = rne_f32(1 / rne_f32(1 + e))
+    a = rne_f32(F(g) * sg) if act == oracle_pkg.ACT_SILU else sg
+    return rne_f32(a * F(u))
+
+
+def pin_gated_act_exact(o):
+    """SiLU/Sigmoid -> Mul against exact rational arithmetic with binary32
+    rounding after each step, exp correctly rounded (page "ggml operator
+    extensions", SiLU/Sigmoid -> Mul -> ConvRot): binary32 and bf16 rows."""
+    rng = np.random.default_rng(72)
+    M, K = 3, 40
+    G = (rng.standard_normal((M, K)) * 4.0).astype(np.float32)
+    U = (rng.standard_normal((M, K)) * 2.0).astype(np.float32)
+    Gb, Ub = workloads.f32_to_bf16_bits(G), workloads.f32_to_bf16_bits(U)
+    for (gs, us, gw, uw) in ((G, U, G, U), (Gb, Ub, workloads.bf16_bits_to_f32(Gb), workloads.bf16_bits_to_f32(Ub))):
+        for act in (oracle_pkg.ACT_SILU, oracle_pkg.ACT_SIGMOID):
+            Y = o.gated_act_rows(gs, us, act)
+            for r in range(M):
+                for i in range(K):
+                    assert F_out(Y[r, i]) == gated_exact(gw[r, i], uw[r, i], act), f"({r},{i}) act={act}"
+
+
+def pin_gated_act_closed_forms(o):
+    """sigmoid(0) = 1/2 and silu(0) = 0; silu(g) = g once exp(-g) is below half an
+    ulp of 1 (g >= 17); sigmoid of a very negative g is 0; the up factor is
+    indexed like the gate; a packed [gate | up] row and its swapped form read
+    the right halves."""
+    K = 64
+    one = np.ones((1, K), np.float32)
+    assert np.array_equal(o.gated_act_rows(np.zeros((1, K), np.float32), one, oracle_pkg.ACT_SIGMOID), 0.5 * one)
+    assert np.array_equal(o.gated_act_rows(np.zeros((1, K), np.float32), one, oracle_pkg.ACT_SILU), 0 * one)
+    big = np.linspace(17.0, 80.0, K, dtype=np.float32)[None, :]
+    assert np.array_equal(o.gated_act_rows(big, one, oracle_pkg.ACT_SILU), big)
+    assert np.all(o.gated_act_rows(-big - 100.0, one, oracle_pkg.ACT_SIGMOID) == 0.0)
+    rng = np.random.default_rng(73)
+    g = rng.standard_normal((2, K)).astype(np.float32)
+    u = rng.standard_normal((2, K)).astype(np.float32)
+    base = o.gated_act_rows(g, u, oracle_pkg.ACT_SILU)
+    packed = np.concatenate([g, u], axis=1)
+    assert np.array_equal(o.gated_act_rows(packed, np.ascontiguousarray(packed[:, K:]), oracle_pkg.ACT_SILU, K=K), base)
+    swapped = np.concatenate([u, g], axis=1)
+    assert np.array_equal(o.gated_act_rows(np.ascontiguousarray(swapped[:, K:]), swapped, oracle_pkg.ACT_SILU, K=K), base)
+    ones = o.gated_act_rows(g, np.ones_like(g), oracle_pkg.ACT_SIGMOID)
+    assert np.array_equal(o.gated_act_rows(g, 2 * np.ones_like(g), oracle_pkg.ACT_SIGMOID), 2 * ones)
+
+
+def pin_gated_act_fp64_bound(o):
+    """Against g / (1 + exp(-g)) * u and u / (1 + exp(-g)) in binary64: within
+    five binary32 roundings."""
+    rng = np.random.default_rng(74)
+    G = (rng.standard_normal((4, 256)) * 6.0).astype(np.float32)
+    U = rng.standard_normal((4, 256)).astype(np.float32)
+    g64, u64 = G.astype(np.float64), U.astype(np.float64)
+    sg = 1.0 / (1.0 + np.exp(-g64))
+    for act, ref in ((oracle_pkg.ACT_SILU, g64 * sg * u64), (oracle_pkg.ACT_SIGMOID, sg * u64)):
+        got = o.gated_act_rows(G, U, act).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 5 * U32 * np.abs(ref) + 1e-38), f"act={act}"
 
 
 def load_int4_golden():

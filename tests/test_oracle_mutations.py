@@ -69,6 +69,12 @@ MUTATIONS = {
     "rms_abs_not_square": ("sq[i] = x * x;", "sq[i] = fabsf(x);"),
     "rms_weight_reversed": ("y = y * weight[i];", "y = y * weight[K - 1 - i];"),
     "rms_last_block_only": ("S = b == 0 ? block : S + block;", "S = block;"),
+    "act_exp_sign": ("const float e = oracle_expf(-g);", "const float e = oracle_expf(g);"),
+    "act_no_one": ("const float d = 1.0f + e;", "const float d = e;"),
+    "act_silu_is_sigmoid": ("const float a = act == ORACLE_ACT_SILU ? g * sg : sg;", "const float a = sg;"),
+    "act_no_up": ("Y[r * K + i] = a * u;", "Y[r * K + i] = a;"),
+    "act_exp_binary32_series": ("return (float)expl((long double)x);",
+                                "return 1.0f + x * (1.0f + x * (0.5f + x * (1.0f / 6.0f)));"),
 }
 
 
