@@ -59,12 +59,13 @@ def source_hash(path: str) -> str:
 
 def quantize_bytes(w: workloads.Workload) -> int:
     """Algorithmic bytes of one quantize pass: read X once (and the producer's
-    per-channel vectors, if any: RMSNorm weight, Modulate scale and shift),
-    write the packed tensor."""
+    inputs, if any: the gated activation's second tensor, the RMSNorm weight,
+    the Modulate scale and shift), write the packed tensor."""
     esz = 2 if w.x_dtype == workloads.BF16 else 4
     m_pad = (w.M + 3) // 4 * 4
     mod = (8 * w.K if w.modulate else 0) + (4 * w.K if w.rmsnorm else 0)
-    return w.M * w.K * esz + m_pad * w.K + 4 * m_pad + mod
+    up = w.M * w.K * esz if w.glu else 0
+    return w.M * w.K * esz + up + m_pad * w.K + 4 * m_pad + mod
 
 
 def gemm_ops(w: workloads.Workload, n_linears: int) -> int:
@@ -162,6 +163,8 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
     X = np.ascontiguousarray(inp.X[:rows])
     t0 = time.perf_counter()
+    if w.glu:
+        X = o.gated_act_rows(X, np.ascontiguousarray(inp.up[:rows]), w.glu, threads=threads)
     if w.rmsnorm:
         X = o.rmsnorm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
     if w.modulate:
@@ -175,7 +178,8 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     dt = time.perf_counter() - t0
     ops = 2 * rows * w.N * w.K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.M} rows of {w.name} ({'RMSNorm + ' if w.rmsnorm else ''}"
+            "sample": f"{rows} of {w.M} rows of {w.name} ({'gated activation + ' if w.glu else ''}"
+                      f"{'RMSNorm + ' if w.rmsnorm else ''}"
                       f"{'modulate + ' if w.modulate else ''}"
                       f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''} "
                       f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
@@ -245,12 +249,16 @@ def main() -> int:
     ybytes = 2 if yd == cr.BF16 else 4
     shared = w.n_linears > 1
     n_packed = len(set(w.input_scales))
-    set_bytes = (inp.X.nbytes + cr.convrot_workspace_bytes(w.M, w.K, n_packed)
+    set_bytes = (inp.X.nbytes * (2 if w.glu else 1) + cr.convrot_workspace_bytes(w.M, w.K, n_packed)
                  + w.n_linears * w.M * w.N * ybytes)
     n_sets = args.sets or max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
     sets = []
+    ups = []                       # the gated activation's second input, per set
     for s in range(n_sets):
-        X = inp.X if s == 0 else workloads.make_inputs(w, seed=w.seed + 1000 * s).X
+        extra = inp if s == 0 else workloads.make_inputs(w, seed=w.seed + 1000 * s)
+        X = extra.X
+        if w.glu:
+            ups.append(to_dev_x(extra.up, torch))
         Xd = to_dev_x(X, torch)
         ws = torch.empty(cr.convrot_workspace_bytes(w.M, w.K, n_packed), dtype=torch.uint8,
                          device=dev)
@@ -268,7 +276,10 @@ def main() -> int:
 
     def quantize(i):
         Xd, ws, Ys = sets[i % n_sets]
-        if mod is not None:
+        if w.glu:
+            cr.convrot_quantize_rows_pre(Xd, cr.GatedAct(ups[i % n_sets], w.glu), w.G,
+                                         lins[0]["input_scale"], packed=ws)
+        elif mod is not None:
             cr.convrot_quantize_rows_pre(Xd, mod, w.G, lins[0]["input_scale"], packed=ws)
         else:
             cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
@@ -351,6 +362,7 @@ def main() -> int:
         "config": {"workload": f"{w.name}: X {w.x_dtype} [{w.M},{w.K}], W {'i4' if w.w_bits == 4 else 'i8'} [{w.N},{w.K}] x "
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
                                f"{list(w.input_scales)}"
+                               + (", SiLU(X) * up fused" if w.glu == 1 else ", Sigmoid(X) * up fused" if w.glu else "")
                                + (", RMSNorm -> Mul(weight) fused" if w.rmsnorm else "")
                                + (", Modulate producer fused" if w.modulate else "")
                                + (", gated residual in place" if w.gated else ""),

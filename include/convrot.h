@@ -183,12 +183,28 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
  * scale: no modulation; shift requires scale).  eps is finite and >= 0;
  * inputs whose squares or sums overflow binary32 are outside the contract.
  * Rows are limited to half the quantizer's K (32768 when K % 256 == 0), else
- * CONVROT_EUNSUPPORTED. */
+ * CONVROT_EUNSUPPORTED.
+ *
+ * CONVROT_PRE_GATED_ACT (same page and section: SiLU/Sigmoid -> Mul ->
+ * ConvRot, and SwiGLU -> ConvRot with packed, swapped or separate gate/up
+ * inputs): with g the quantizer's input X and u = up[r][i], a second tensor
+ * of X's dtype and row stride ld_up (elements; ld_up * element size a
+ * multiple of 16, up 16-byte aligned):
+ *     sigmoid(g) = fl(1 / fl(1 + e)),  e = exp(-g) correctly rounded
+ *     act = CONVROT_ACT_SIGMOID: a = sigmoid(g)
+ *     act = CONVROT_ACT_SILU:    a = fl(g * sigmoid(g))
+ *     x' = fl(a * u)
+ * A packed [gate | up] row of 2K features is X = base, up = base + K with
+ * ldx = ld_up = 2K (swapped: the other way round).  up may overlap X; packed
+ * must not overlap it.  Same row limit as RMSNORM_MODULATE. */
 typedef enum {
     CONVROT_PRE_NONE = 0,
     CONVROT_PRE_MODULATE = 1,
-    CONVROT_PRE_RMSNORM_MODULATE = 2
+    CONVROT_PRE_RMSNORM_MODULATE = 2,
+    CONVROT_PRE_GATED_ACT = 3
 } convrot_pre_kind;
+
+typedef enum { CONVROT_ACT_SILU = 1, CONVROT_ACT_SIGMOID = 2 } convrot_act;
 
 typedef struct {
     int kind;                  /* convrot_pre_kind */
@@ -196,6 +212,9 @@ typedef struct {
     const float *shift;        /* [K] (device) or NULL */
     const float *norm_weight;  /* RMSNORM_MODULATE: [K] (device) or NULL */
     float eps;                 /* RMSNORM_MODULATE: added to the mean square */
+    const void *up;            /* GATED_ACT: [M][ld_up] (device), X's dtype */
+    int64_t ld_up;             /* GATED_ACT: elements, >= K */
+    int act;                   /* GATED_ACT: convrot_act */
 } convrot_pre;
 
 /* convrot_quantize_rows with a producer.  pre may be NULL or of kind
@@ -271,6 +290,13 @@ int int4_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
  * kernel as int4_linear); A is [M][N] int32. */
 int convrot_int4_gemm_i32(const int8_t *Qx, const uint8_t *W4, int64_t M, int64_t K, int64_t N,
                           int32_t *A, void *stream);
+
+/* The correctly rounded binary32 exp of CONVROT_PRE_GATED_ACT, elementwise:
+ * y[i] = exp(x[i]) for n device floats (0 below -104, +inf above 89; inputs
+ * finite).  y may be x itself (in place); any other overlap is
+ * CONVROT_EOVERLAP.  Exposed so that the device build of the exp can be
+ * checked against a reference directly. */
+int convrot_expf(const float *x, float *y, int64_t n, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *convrot_status_string(int status);

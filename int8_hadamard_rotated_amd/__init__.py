@@ -16,7 +16,8 @@ LIBRARY = os.path.join(_HERE, "libconvrot.so")
 
 OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
-PRE_NONE, PRE_MODULATE, PRE_RMSNORM_MODULATE = 0, 1, 2
+PRE_NONE, PRE_MODULATE, PRE_RMSNORM_MODULATE, PRE_GATED_ACT = 0, 1, 2, 3
+ACT_SILU, ACT_SIGMOID = 1, 2
 POST_NONE, POST_GATED_RESIDUAL = 0, 1
 MAX_LINEARS = 16
 
@@ -51,6 +52,9 @@ class PreDesc(ctypes.Structure):
         ("shift", ctypes.c_void_p),
         ("norm_weight", ctypes.c_void_p),
         ("eps", ctypes.c_float),
+        ("up", ctypes.c_void_p),
+        ("ld_up", ctypes.c_int64),
+        ("act", ctypes.c_int),
     ]
 
 
@@ -80,6 +84,19 @@ class RMSNormModulate:
         ptr = lambda t: None if t is None else t.data_ptr()
         return PreDesc(PRE_RMSNORM_MODULATE, ptr(self.scale), ptr(self.shift), ptr(self.weight),
                        self.eps)
+
+
+class GatedAct:
+    """fl(act(x) * up) ahead of the quantizer (act: ACT_SILU or ACT_SIGMOID);
+    up is a device tensor of X's dtype with K columns in use (a packed
+    [gate | up] tensor gives both halves as views)."""
+
+    def __init__(self, up, act: int = ACT_SILU):
+        self.up, self.act = up, act
+
+    def desc(self) -> PreDesc:
+        return PreDesc(PRE_GATED_ACT, None, None, None, 0.0, self.up.data_ptr(),
+                       _row_stride(self.up), self.act)
 
 
 class PostDesc(ctypes.Structure):
@@ -146,6 +163,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                                    ctypes.POINTER(PostDesc), vp, i32, i64, vp]),
         "convrot_int4_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "convrot_status_string": (ctypes.c_char_p, [i32]),
+        "convrot_expf": (i32, [vp, vp, i64, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -322,6 +340,17 @@ def convrot_int4_gemm_i32(Qx, W4, A=None, M: int | None = None, stream=None):
     rc = library().convrot_int4_gemm_i32(_ptr(Qx), _ptr(W4), M, K, N, _ptr(A), _stream(stream, A))
     _check("convrot_int4_gemm_i32", rc)
     return A
+
+
+def convrot_expf(x, y=None, stream=None):
+    """Correctly rounded binary32 exp of a float32 device tensor (the gated
+    activation's exp); y may be x."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty_like(x)
+    rc = library().convrot_expf(_ptr(x), _ptr(y), x.numel(), _stream(stream, x))
+    _check("convrot_expf", rc)
+    return y
 
 
 def convrot_int8_gemm_i32(Qx, Qw, A=None, M: int | None = None, stream=None):

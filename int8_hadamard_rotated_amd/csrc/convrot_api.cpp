@@ -155,16 +155,40 @@ int out_kind_of(int y_dtype) { return y_dtype == CONVROT_BF16 ? kOutBF16 : kOutF
 // Validates a producer descriptor (nullable) and returns the spans it reads.
 // The producer's device vectors, for overlap checks.
 struct PreSpans {
-    Span scale, shift, weight;
-    bool hits(const Span &s) const { return overlap(scale, s) || overlap(shift, s) || overlap(weight, s); }
+    Span scale, shift, weight, up;
+    bool hits(const Span &s) const
+    {
+        return overlap(scale, s) || overlap(shift, s) || overlap(weight, s) || overlap(up, s);
+    }
 };
 
-int check_pre(const convrot_pre *pre, int64_t K, PreOp *op, PreSpans *spans)
+// The gated activation: a second input of X's dtype and shape.
+int check_gated_act(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, PreOp *op,
+                    PreSpans *spans)
+{
+    if (pre->act != CONVROT_ACT_SILU && pre->act != CONVROT_ACT_SIGMOID)
+        return CONVROT_EUNSUPPORTED;
+    const int64_t esz = elem_bytes(x_dtype);
+    if (!pre->up || !aligned(pre->up, 16) || pre->ld_up < K || (pre->ld_up * esz) % 16 != 0)
+        return CONVROT_EINVAL;
+    if (K > quantize_max_k(K, true))
+        return CONVROT_EUNSUPPORTED;
+    op->kind = kPreGatedAct;
+    op->up = pre->up;
+    op->ld_up = pre->ld_up;
+    op->act = pre->act == CONVROT_ACT_SILU ? kActSilu : kActSigmoid;
+    spans->up = M > 0 ? rows_span(pre->up, M, K, pre->ld_up, esz) : Span{};
+    return CONVROT_OK;
+}
+
+int check_pre(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, PreOp *op, PreSpans *spans)
 {
     *op = PreOp{};
     *spans = PreSpans{};
     if (!pre || pre->kind == CONVROT_PRE_NONE)
         return CONVROT_OK;
+    if (pre->kind == CONVROT_PRE_GATED_ACT)
+        return check_gated_act(pre, M, K, x_dtype, op, spans);
     if (pre->kind != CONVROT_PRE_MODULATE && pre->kind != CONVROT_PRE_RMSNORM_MODULATE)
         return CONVROT_EUNSUPPORTED;
     const bool rms = pre->kind == CONVROT_PRE_RMSNORM_MODULATE;
@@ -216,7 +240,7 @@ int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, 
         return rc;
     PreOp op;
     PreSpans ps;
-    rc = check_pre(pre, K, &op, &ps);
+    rc = check_pre(pre, M, K, x_dtype, &op, &ps);
     if (rc != CONVROT_OK)
         return rc;
     if (M == 0)
@@ -229,6 +253,20 @@ int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, 
     (void)hipGetLastError();
     return hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, input_scale, op, packed,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int convrot_expf(const float *x, float *y, int64_t n, void *stream)
+{
+    if (n < 0)
+        return CONVROT_EINVAL;
+    if (n == 0)
+        return CONVROT_OK;
+    if (!x || !y || !aligned(x, 4) || !aligned(y, 4) || n > ((int64_t)1 << 38))
+        return CONVROT_EINVAL;
+    if (x != y && overlap(span_of(x, 4 * n), span_of(y, 4 * n)))
+        return CONVROT_EOVERLAP;
+    (void)hipGetLastError();
+    return hip_status(launch_expf(x, y, n, static_cast<hipStream_t>(stream)));
 }
 
 int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -415,7 +453,7 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
         return rc;
     PreOp op;
     PreSpans ps;
-    rc = check_pre(pre, K, &op, &ps);
+    rc = check_pre(pre, M, K, x_dtype, &op, &ps);
     if (rc != CONVROT_OK)
         return rc;
     rc = check_contraction_k(K);

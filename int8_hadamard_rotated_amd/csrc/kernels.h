@@ -14,7 +14,8 @@ namespace convrot_detail {
 int64_t quantize_max_k(int64_t K, bool rmsnorm = false);
 
 // Producer applied to each widened input element before the rotation.
-enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2 };
+enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2, kPreGatedAct = 3 };
+enum ActKind : int { kActSilu = 1, kActSigmoid = 2 };
 
 struct PreOp {
     int kind = kPreNone;
@@ -22,7 +23,13 @@ struct PreOp {
     const float *shift = nullptr;         // per-channel [K] or null (needs scale)
     const float *norm_weight = nullptr;   // kPreRmsNormModulate: per-channel [K] or null
     float eps = 0.0f;                     // kPreRmsNormModulate
+    const void *up = nullptr;             // kPreGatedAct: [M][ld_up], X's dtype
+    int64_t ld_up = 0;
+    int act = 0;                          // kPreGatedAct: ActKind
 };
+
+// y[i] = correctly rounded exp(x[i]) (the gated activation's exp).
+hipError_t launch_expf(const float *x, float *y, int64_t n, hipStream_t stream);
 
 // Launch the (producer +) rotate + row-max + quantize + pack kernel.
 // Arguments are already validated (see convrot_quantize_rows_pre).

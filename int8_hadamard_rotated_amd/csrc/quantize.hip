@@ -7,6 +7,9 @@
 //                                           "ggml operator extensions", section
 //                                           "sd.cpp integration"; per-channel
 //                                           vectors, shift optional)
+//   x  = fl(act(x) * u)                    (optional gated activation, SiLU or
+//                                           Sigmoid of x times a second input
+//                                           u, same page and section)
 //   x  = fl(x * r) [* w]                   (optional RMSNorm -> Mul(weight)
 //                                           ahead of Modulate, same page and
 //                                           section; r per row, see below)
@@ -52,6 +55,7 @@
 // code), whose low byte is the two's-complement int8 code.
 #pragma clang fp contract(off)
 
+#include "expf_cr.h"
 #include "kernels.h"
 
 namespace convrot_detail {
@@ -250,6 +254,21 @@ __device__ __forceinline__ void weight8(float (&v)[8], const float *__restrict__
         v[p] = v[p] * wv[p];
 }
 
+// The gated activation on one value: sigmoid(g) = fl(1 / fl(1 + exp(-g)))
+// with exp correctly rounded; SiLU is fl(g * sigmoid(g)).  Division by IEEE
+// rule (the toolchain's default single-precision division is correctly
+// rounded).
+template <int ACT>
+__device__ __forceinline__ float gated_act(float g)
+{
+    const float e = convrot_expf::expf_cr(-g);
+    const float d = 1.0f + e;
+    const float sg = __fdiv_rn(1.0f, d);
+    if constexpr (ACT == kActSilu)
+        return g * sg;
+    return sg;
+}
+
 // Codes of one chunk: rne(fl(y * inv)) in two's complement, 8 bytes.
 __device__ __forceinline__ v2u encode8(const float (&v)[8], float inv)
 {
@@ -316,13 +335,18 @@ __device__ __forceinline__ void modulate8(float (&v)[8], const float *__restrict
 // r = fl(1 / fl(sqrt(fl(fl(S / K) + eps)))) with correctly rounded operations;
 // every lane then scales its values by its row's r (and the weight).
 //
-// With RMSNorm the workgroup has at most 512 threads (two waves per SIMD), so
-// that the row data, the block sums and the vectors fit in registers.
-template <typename XT, int G, int NC, bool SCALED, int MOD, bool RMS>
-__global__ __launch_bounds__(RMS ? 512 : 1024) void quantize_rows_kernel(
+// With RMSNorm or a gated activation the workgroup has at most 512 threads
+// (two waves per SIMD), so that the row data, the block sums or the exp's
+// binary64 temporaries fit in registers.
+//
+// A gated activation (ACT != 0) reads the second input up with the same
+// lane layout as X and replaces each value by fl(act(x) * u) right after
+// widening.
+template <typename XT, int G, int NC, bool SCALED, int MOD, bool RMS, int ACT>
+__global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_kernel(
     const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
     const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
-    const float *__restrict__ norm_weight, float eps,
+    const float *__restrict__ norm_weight, float eps, const XT *__restrict__ up, int64_t ld_up,
     int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
@@ -337,6 +361,7 @@ __global__ __launch_bounds__(RMS ? 512 : 1024) void quantize_rows_kernel(
     const int j0 = tid & 1, j1 = (tid >> 1) & 1;
     int row_local, q_in_row;
     quad_place<(MOD != 0 || RMS) ? 1 : 0>(quad, quads_per_row, rows_per_wg, row_local, q_in_row);
+    static_assert(ACT == 0 || (MOD == 0 && !RMS), "one producer at a time");
     const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
     const int64_t span0 = (int64_t)q_in_row * (32 * NC);
     // A quad never straddles rows, so this branch is uniform per quad and the
@@ -353,6 +378,17 @@ __global__ __launch_bounds__(RMS ? 512 : 1024) void quantize_rows_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             load8(xr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1), v[c]);
+        if constexpr (ACT != 0) {
+            const XT *ur = up + row * ld_up + span0;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float u[8];
+                load8(ur + chunk_offset(j0, j1, c), u);
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    v[c][p] = gated_act<ACT>(v[c][p]) * u[p];
+            }
+        }
     }
     if constexpr (RMS) {
         const int row_blocks = quads_per_row * kBlocks;
@@ -607,13 +643,13 @@ int gcd_int(int a, int b)
     return a;
 }
 
-template <typename XT, int G, int NC, int MOD, bool RMS>
+template <typename XT, int G, int NC, int MOD, bool RMS, int ACT>
 void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                   void *packed, hipStream_t stream)
 {
     const int64_t m_pad = (M + 3) / 4 * 4;
     const int qr = (int)(K / (32 * NC));
-    constexpr int kMaxThreads = RMS ? 512 : 1024;
+    constexpr int kMaxThreads = (RMS || ACT != 0) ? 512 : 1024;
     // smallest row count that fills whole waves, then grow towards 256 threads
     int rows = 16 / gcd_int(qr, 16);
     if (4 * qr * rows > kMaxThreads)
@@ -624,47 +660,50 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
     const int64_t blocks = (m_pad + rows - 1) / rows;
     int8_t *Q = static_cast<int8_t *>(packed);
     float *S = reinterpret_cast<float *>(Q + m_pad * K);
-    if constexpr (sizeof(XT) == 4 && !RMS) {
+    if constexpr (sizeof(XT) == 4 && !RMS && ACT == 0) {
         // binary32 rows of up to 256 threads per workgroup take the staged kernel
         if (threads <= 256)
             return launch_staged<G, NC, MOD>(static_cast<const float *>(X), M, K, ldx, alpha, pre, Q,
                                              S, m_pad, qr, rows, stream);
     }
+    const XT *up = static_cast<const XT *>(pre.up);
     if (alpha != 1.0f)
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
+                           qr, rows);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, RMS>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT>), dim3((unsigned)blocks),
                            dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
-                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, Q, S, qr, rows);
+                           alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
+                           qr, rows);
 }
 
-template <typename XT, int NC, int MOD, bool RMS>
+template <typename XT, int NC, int MOD, bool RMS, int ACT>
 void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
-    case 4: launch_typed<XT, 4, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 16: launch_typed<XT, 16, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 64: launch_typed<XT, 64, NC, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 4: launch_typed<XT, 4, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 16: launch_typed<XT, 16, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 64: launch_typed<XT, 64, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
     default:
         if constexpr (NC == 8)
-            launch_typed<XT, 256, 8, MOD, RMS>(X, M, K, ldx, alpha, pre, packed, stream);
+            launch_typed<XT, 256, 8, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
         break;
     }
 }
 
-template <typename XT, int MOD, bool RMS>
+template <typename XT, int MOD, bool RMS, int ACT>
 void launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                   const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (K % 256 == 0)
-        launch_nc<XT, 8, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 8, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else if (K % 128 == 0)
-        launch_nc<XT, 4, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 4, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_nc<XT, 2, MOD, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_nc<XT, 2, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT, bool RMS>
@@ -672,11 +711,11 @@ void launch_mod(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float a
                 const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (pre.scale && pre.shift)
-        launch_dtype<XT, 2, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_dtype<XT, 2, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else if (pre.scale)
-        launch_dtype<XT, 1, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_dtype<XT, 1, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
-        launch_dtype<XT, 0, RMS>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        launch_dtype<XT, 0, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT>
@@ -685,8 +724,20 @@ void launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float a
 {
     if (pre.kind == kPreRmsNormModulate)
         launch_mod<XT, true>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else if (pre.kind == kPreGatedAct && pre.act == kActSilu)
+        launch_dtype<XT, 0, false, kActSilu>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    else if (pre.kind == kPreGatedAct)
+        launch_dtype<XT, 0, false, kActSigmoid>(G, X, M, K, ldx, alpha, pre, packed, stream);
     else
         launch_mod<XT, false>(G, X, M, K, ldx, alpha, pre, packed, stream);
+}
+
+// y may be x (each lane reads its element before writing it).
+__global__ __launch_bounds__(256) void expf_kernel(const float *x, float *y, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        y[i] = convrot_expf::expf_cr(x[i]);
 }
 
 }  // namespace
@@ -701,6 +752,13 @@ int64_t quantize_max_k(int64_t K, bool rmsnorm)
     if (K % 128 == 0)
         return quads * 128;
     return quads * 64;
+}
+
+hipError_t launch_expf(const float *x, float *y, int64_t n, hipStream_t stream)
+{
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(expf_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,

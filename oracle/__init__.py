@@ -102,6 +102,7 @@ class Oracle:
             "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
             "oracle_rmsnorm_rows": (i32, [vp, i32, i64, i64, i64, f32, vp, vp, i32]),
             "oracle_expf": (f32, [f32]),
+            "oracle_expf_array": (i32, [vp, vp, i64, i32]),
             "oracle_gated_act_rows": (i32, [vp, i32, i64, i64, i64, vp, i64, i32, vp, i32]),
             "oracle_unpack_int4": (i32, [vp, i64, i64, vp]),
             "oracle_gated_residual": (i32, [vp, i64, i64, f32, vp, vp, i32, i64, i32, vp, i64, i32]),
@@ -186,6 +187,12 @@ class Oracle:
     def expf(self, x: float) -> float:
         """exp rounded once to binary32 (the oracle's exp)."""
         return float(self.lib.oracle_expf(ctypes.c_float(x)))
+
+    def expf_array(self, x: np.ndarray, threads: int = 1) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        y = np.empty_like(x)
+        self._check(self.lib.oracle_expf_array(_p(x), _p(y), x.size, threads), "expf_array")
+        return y
 
     def gated_act_rows(self, X: np.ndarray, U: np.ndarray, act: int, K: int | None = None,
                        threads: int = 1) -> np.ndarray:

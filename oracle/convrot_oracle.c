@@ -360,6 +360,17 @@ float oracle_expf(float x)
     return (float)expl((long double)x);
 }
 
+/* oracle_expf over n values (for checking other builds of exp in bulk). */
+int oracle_expf_array(const float *x, float *y, int64_t n, int threads)
+{
+    if (n < 0 || (n > 0 && (!x || !y)))
+        return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = oracle_expf(x[i]);
+    return ORACLE_OK;
+}
+
 #define ORACLE_ACT_SILU 1
 #define ORACLE_ACT_SIGMOID 2
 

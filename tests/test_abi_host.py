@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
         "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
-        "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post"])
+        "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -127,6 +127,21 @@ def test_producer_validation(lib):
     assert qpre(lib, kind=rms, w=w + 8) == EINVAL
     assert qpre(lib, kind=rms, w=BASE + 64 * MB + 1024) == EOVL        # packed overlaps the weight
     assert qpre(lib, kind=rms, w=w, K=32768 + 256) == EUNSUP
+    # gated activation: a second input with X's dtype, aligned, with a valid
+    # stride, that packed does not overlap; SiLU or Sigmoid; same row limit
+    def qact(up=BASE + 100 * MB, ld=256, act=cr.ACT_SILU, M=8, K=256, packed=BASE + 64 * MB):
+        d = cr.PreDesc(cr.PRE_GATED_ACT, None, None, None, 0.0, up, ld, act)
+        return lib.convrot_quantize_rows_pre(ctypes.c_void_p(BASE), cr.F32, M, K, K, ctypes.byref(d),
+                                             16, ctypes.c_float(1.0), ctypes.c_void_p(packed), None)
+    assert qact(M=0) == OK
+    assert qact(up=BASE, M=0) == OK                                     # up may alias X
+    assert qact(act=3) == EUNSUP
+    assert qact(up=0) == EINVAL
+    assert qact(up=BASE + 100 * MB + 4) == EINVAL
+    assert qact(ld=200) == EINVAL                                       # below K
+    assert qact(ld=257) == EINVAL                                       # stride not 16-byte
+    assert qact(up=BASE + 64 * MB + 256) == EOVL                        # packed overlaps up
+    assert qact(K=32768 + 256, ld=32768 + 256) == EUNSUP
     # the shared entry: the workspace must not overlap the vectors
     d = cr.LinearDesc(BASE + 16 * MB, None, None, 32, 1.0, BASE + 32 * MB, cr.F32, 32)
     pre = cr.PreDesc(cr.PRE_RMSNORM_MODULATE, None, None, BASE + 48 * MB + 512, 1e-6)
@@ -140,6 +155,15 @@ def test_producer_validation(lib):
     pre.kind = 9
     assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),
              ctypes.c_void_p(BASE + 48 * MB), MB, None) == EUNSUP
+
+
+def test_expf_validation(lib):
+    f = lib.convrot_expf
+    assert f(None, None, 0, None) == OK
+    assert f(None, ctypes.c_void_p(BASE), 4, None) == EINVAL
+    assert f(ctypes.c_void_p(BASE + 2), ctypes.c_void_p(BASE + MB), 4, None) == EINVAL
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + 8), 4, None) == EOVL
+    assert f(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + MB), -1, None) == EINVAL
 
 
 def lin(lib, Qx=BASE, sx=BASE + 8 * MB, M=8, K=256, Qw=BASE + 16 * MB, sw=BASE + 24 * MB,

@@ -28,6 +28,8 @@ Recipe, per workload (fixed draw order):
     when the workload has a gated-residual epilogue:
         gate = rng.standard_normal(N, float32) * 0.3
         residual = rng.standard_normal((M, N), float32), in the output dtype
+    when the workload has a gated activation producer (X is the gate):
+        up = rng.standard_normal((M, K), float32), outliers as for X, same dtype
     when the workload has an RMSNorm -> Mul(weight) producer (eps 1e-6):
         norm_weight = 1 + rng.standard_normal(K, float32) * 0.1
     when the workload has a Modulate producer (per-channel vectors, as the
@@ -63,6 +65,7 @@ class Workload:
     gated: bool = False               # a gated-residual epilogue after the linear
     rmsnorm: bool = False             # RMSNorm -> Mul(weight) ahead of the Modulate
     rms_eps: float = 1e-6
+    glu: int = 0                      # 1 SiLU, 2 Sigmoid: fl(act(X) * up) ahead of the rotation
     note: str = ""
 
     @property
@@ -91,6 +94,8 @@ WORKLOADS = {
     "proj_gated": Workload("proj_gated", 4096, 3072, 3072, 256, BF16, BF16, (1.0,), seed=7,
                            gated=True,
                            note="DiT output projection with its gated residual, in place"),
+    "mlp_down_glu": Workload("mlp_down_glu", 4096, 12288, 3072, 256, BF16, BF16, (1.0,), seed=9,
+                             glu=1, note="DiT MLP down-projection of silu(gate) * up, fused"),
     "mlp_down": Workload("mlp_down", 16384, 12288, 3072, 256, BF16, BF16, (1.0,), seed=4,
                          note="batched MLP down-projection, 4 images x 4096 tokens, bf16 in/out"),
 }
@@ -140,6 +145,7 @@ class Inputs:
     b: list = field(default_factory=list)   # float32 [N] per linear
     s_w: list = field(default_factory=list) # float32 [N] per linear (4-bit weights only)
     norm_weight: np.ndarray | None = None   # float32 [K] (RMSNorm producer)
+    up: np.ndarray | None = None            # like X, [M,K] (gated activation producer)
     mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
     mod_shift: np.ndarray | None = None     # float32 [K]
     gate: np.ndarray | None = None          # float32 [N] (gated residual)
@@ -164,6 +170,8 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
         W, b = gaussian_weights(rng, w.N, w.K)
         inp.W.append(W)
         inp.b.append(b)
+    if w.glu:
+        inp.up = gaussian_activations(rng, rows, w.K, w.outlier_p, w.outlier_f, w.x_dtype)
     if w.rmsnorm:
         inp.norm_weight = norm_weight(rng, w.K)
     if w.modulate:
