@@ -169,19 +169,26 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
         X = o.rmsnorm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
     if w.modulate:
         X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
-    if w.gated:
+    if w.swiglu:
+        Qu, su = o.weight_prep(inp.W[1], w.G, threads=threads)      # untimed
+        t0 = time.perf_counter()
+        Yg = o.linear(X, w.G, Qw, sw, None, w.input_scales[0], oracle.F32, threads=threads)
+        Yu = o.linear(X, w.G, Qu, su, None, w.input_scales[0], oracle.F32, threads=threads)
+        o.gated_act_rows(Yg, Yu, oracle.ACT_SILU, threads=threads)
+    elif w.gated:
         Yf = o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], oracle.F32, threads=threads)
         o.gated_residual(Yf, inp.gate, np.ascontiguousarray(inp.residual[:rows]), 1.0, yd,
                          threads=threads)
     else:
         o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
     dt = time.perf_counter() - t0
-    ops = 2 * rows * w.N * w.K
+    ops = 2 * rows * w.N * w.K * (2 if w.swiglu else 1)
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {w.M} rows of {w.name} ({'gated activation + ' if w.glu else ''}"
                       f"{'RMSNorm + ' if w.rmsnorm else ''}"
                       f"{'modulate + ' if w.modulate else ''}"
-                      f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''} "
+                      f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''}"
+                      f"{' for the gate and up weights + SwiGLU' if w.swiglu else ''} "
                       f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
 
 
@@ -247,7 +254,7 @@ def main() -> int:
 
     yd = cr.BF16 if w.y_dtype == workloads.BF16 else cr.F32
     ybytes = 2 if yd == cr.BF16 else 4
-    shared = w.n_linears > 1
+    shared = w.n_linears > 1 and not w.swiglu
     n_packed = len(set(w.input_scales))
     set_bytes = (inp.X.nbytes * (2 if w.glu else 1) + cr.convrot_workspace_bytes(w.M, w.K, n_packed)
                  + w.n_linears * w.M * w.N * ybytes)
@@ -293,6 +300,11 @@ def main() -> int:
         if w.gated:
             cr.int8_linear_post(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"],
                                 cr.GatedResidual(gate, Ys[0]), Y=Ys[0], M=w.M)
+            return
+        if w.swiglu:
+            u = lins[1]
+            cr.int8_swiglu_linear(qx, sx, l["Qw"], l["s_w"], u["Qw"], u["s_w"], l["input_scale"],
+                                  Y=Ys[0], M=w.M)
             return
         lin_fn = cr.int4_linear if w.w_bits == 4 else cr.int8_linear
         lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
@@ -363,6 +375,7 @@ def main() -> int:
                                f"{w.n_linears}, G={w.G}, Y {w.y_dtype}, input scales "
                                f"{list(w.input_scales)}"
                                + (", SiLU(X) * up fused" if w.glu == 1 else ", Sigmoid(X) * up fused" if w.glu else "")
+                               + (", one dual GEMM with the SwiGLU epilogue (gate, up)" if w.swiglu else "")
                                + (", RMSNorm -> Mul(weight) fused" if w.rmsnorm else "")
                                + (", Modulate producer fused" if w.modulate else "")
                                + (", gated residual in place" if w.gated else ""),

@@ -273,6 +273,23 @@ int int8_linear_post(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, c
                      const float *s_w, const float *bias, int64_t N, float input_scale,
                      const convrot_post *post, void *Y, int y_dtype, int64_t ldy, void *stream);
 
+/* Dual GEMM with a SwiGLU epilogue on one packed input (page "ggml operator
+ * extensions", section "sd.cpp integration": GEMM -> SwiGLU [-> ConvRot],
+ * gate and up weights in separate allocations, with their own weight scales,
+ * no bias):
+ *     g = fl(fl(fl(float(Q_x Qw_gate^T)) * s_x) * s_w_gate) [/ input_scale]
+ *     u = fl(fl(fl(float(Q_x Qw_up^T)) * s_x) * s_w_up) [/ input_scale]
+ *     Y = fl(silu(g) * u),  silu(g) = fl(g * fl(1 / fl(1 + exp(-g))))
+ * with exp correctly rounded (the one of CONVROT_PRE_GATED_ACT), then one
+ * cast to y_dtype.  Both weight tensors are [N][K] int8 (16-byte aligned);
+ * the scales are nullable (1).  Y is [M][ldy]; the same rules as int8_linear
+ * for everything else.  Quantize Y with convrot_quantize_rows for the
+ * optional ConvRot of the result. */
+int int8_swiglu_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K,
+                       const int8_t *Qw_gate, const float *s_w_gate, const int8_t *Qw_up,
+                       const float *s_w_up, int64_t N, float input_scale, void *Y, int y_dtype,
+                       int64_t ldy, void *stream);
+
 /* 4-bit weights, format convrot_w4a4 (page "INT8 Convrot Safetensors",
  * section "Packed INT4 convrot"): W4 is [N][K/2] bytes, feature k of output o
  * in byte o*K/2 + k/2, low nibble for even k, high nibble for odd k, each a

@@ -164,6 +164,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
         "convrot_int4_gemm_i32": (i32, [vp, vp, i64, i64, i64, vp, vp]),
         "convrot_status_string": (ctypes.c_char_p, [i32]),
         "convrot_expf": (i32, [vp, vp, i64, vp]),
+        "int8_swiglu_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -340,6 +341,23 @@ def convrot_int4_gemm_i32(Qx, W4, A=None, M: int | None = None, stream=None):
     rc = library().convrot_int4_gemm_i32(_ptr(Qx), _ptr(W4), M, K, N, _ptr(A), _stream(stream, A))
     _check("convrot_int4_gemm_i32", rc)
     return A
+
+
+def int8_swiglu_linear(Qx, s_x, Qw_gate, s_w_gate, Qw_up, s_w_up, input_scale: float = 1.0,
+                       Y=None, y_dtype: int = F32, M: int | None = None, stream=None):
+    """Y = silu(gate reconstruction) * up reconstruction on one packed input."""
+    torch = _torch()
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    N = Qw_gate.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=Qw_gate.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    rc = library().int8_swiglu_linear(_ptr(Qx), _ptr(s_x), M, K, _ptr(Qw_gate), _ptr(s_w_gate),
+                                      _ptr(Qw_up), _ptr(s_w_up), N, ctypes.c_float(input_scale),
+                                      _ptr(Y), _dtype_code(Y), ldy, _stream(stream, Qw_gate))
+    _check("int8_swiglu_linear", rc)
+    return Y
 
 
 def convrot_expf(x, y=None, stream=None):

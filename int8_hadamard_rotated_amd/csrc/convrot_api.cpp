@@ -413,6 +413,46 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
     return linear_impl(Qx, s_x, M, K, Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy, stream, 8);
 }
 
+int int8_swiglu_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K,
+                       const int8_t *Qw_gate, const float *s_w_gate, const int8_t *Qw_up,
+                       const float *s_w_up, int64_t N, float input_scale, void *Y, int y_dtype,
+                       int64_t ldy, void *stream)
+{
+    if (M < 0)
+        return CONVROT_EINVAL;
+    int rc = check_contraction_k(K, 8);
+    if (rc != CONVROT_OK)
+        return rc;
+    LinearCheck cg, cu;
+    rc = check_linear(Qw_gate, s_w_gate, nullptr, M, K, N, input_scale, Y, y_dtype, ldy, true, &cg, 8);
+    if (rc != CONVROT_OK)
+        return rc;
+    rc = check_linear(Qw_up, s_w_up, nullptr, M, K, N, input_scale, Y, y_dtype, ldy, true, &cu, 8);
+    if (rc != CONVROT_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return CONVROT_OK;
+    if (!Qx || !s_x || !aligned(Qx, 16) || !aligned(s_x, 4))
+        return CONVROT_EINVAL;
+    if (overlap(cg.y, span_of(Qx, M * K)) || overlap(cg.y, span_of(s_x, 4 * M)) ||
+        y_hits_weights(cg, cg) || y_hits_weights(cg, cu))
+        return CONVROT_EOVERLAP;
+    GemmProblem p;
+    std::memset(&p, 0, sizeof p);
+    p.Qx = Qx;
+    p.s_x = s_x;
+    p.M = M;
+    p.K = K;
+    p.w_bits = 8;
+    p.n_lin = 1;
+    p.lin[0] = make_linear(Qw_gate, s_w_gate, nullptr, N, input_scale, Y, out_kind_of(y_dtype), ldy);
+    p.lin[0].glu = 1;
+    p.lin[0].Qw_up = Qw_up;
+    p.lin[0].s_w_up = s_w_up;
+    (void)hipGetLastError();
+    return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
 int int8_linear_post(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const int8_t *Qw,
                      const float *s_w, const float *bias, int64_t N, float input_scale,
                      const convrot_post *post, void *Y, int y_dtype, int64_t ldy, void *stream)

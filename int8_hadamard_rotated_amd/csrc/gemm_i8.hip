@@ -26,6 +26,7 @@
 // on one XCD share operand panels in its L2.
 #pragma clang fp contract(off)
 
+#include "expf_cr.h"
 #include "kernels.h"
 
 namespace convrot_detail {
@@ -150,7 +151,11 @@ __device__ __forceinline__ v4i expand_w4(v2u p)
                (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u), (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool DIV, int WB, bool POST>
+// Epilogue kinds: the plain reconstruction, with the gated residual after it,
+// or SwiGLU (silu of one reconstruction times another).
+enum EpiKind : int { kEpiPlain = 0, kEpiPost = 1, kEpiGlu = 2 };
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool DIV, int WB, int EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     GemmProblem p, int tiles_m, int total_tiles)
 {
@@ -174,8 +179,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int tm = first_m + in_group % gsize;
     const int tn = in_group / gsize;
 
+    constexpr bool POST = EPI == kEpiPost;
+    constexpr bool GLU = EPI == kEpiGlu;
+    static_assert(!GLU || WB == 8, "SwiGLU pairs take int8 weights");
     const int64_t M = p.M, K = p.K, N = L.N;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    // SwiGLU: the tile's BN columns are BN/2 outputs.  In every wave's column
+    // block the first half are gate rows and the second half up rows of the
+    // same outputs, so a lane holds the gate and up accumulators of one
+    // output column (blocks j and j + kTN/2).
+    const int64_t n0o = GLU ? (int64_t)tn * (BN / 2) : n0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
@@ -195,9 +208,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // (or N) fall outside it and are never stored.
     const int64_t kb = WB == 4 ? K / 2 : K;                   // weight bytes per row
     const int64_t a_rows = (M - m0) < BM ? (M - m0) : BM;
-    const int64_t b_rows = (N - n0) < BN ? (N - n0) : BN;
+    const int64_t b_span = GLU ? BN / 2 : BN;
+    const int64_t b_rows = (N - n0o) < b_span ? (N - n0o) : b_span;
     const v4u a_rsrc = buffer_rsrc(p.Qx + m0 * K, (uint32_t)(a_rows * K));
-    const v4u b_rsrc = buffer_rsrc(L.Qw + n0 * kb, (uint32_t)(b_rows * kb));
+    const v4u b_rsrc = buffer_rsrc(L.Qw + n0o * kb, (uint32_t)(b_rows * kb));
+    const v4u u_rsrc = buffer_rsrc(GLU ? L.Qw_up + n0o * kb : nullptr, GLU ? (uint32_t)(b_rows * kb) : 0u);
     const int ld_row = lane >> 2;
     const int ld_voff = ld_row * (int)K + 16 * ((lane & 3) ^ swz(ld_row));
     const int ld_voff_b = WB == 4 ? (lane >> 1) * (int)kb + 16 * (lane & 1) : ld_voff;
@@ -212,8 +227,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             dma_x4(a_rsrc, ld_voff, 16 * g * (int)K + step * kBK, st + 1024 * g);
         } else if (g < T::kDma) {
             const int gb = g - T::kDmaA;
-            dma_x4(b_rsrc, ld_voff_b, T::kRowsPerDmaB * gb * (int)kb + step * T::kStrideB,
-                   st + T::kABytes + 1024 * gb);
+            if constexpr (GLU) {
+                // 16 tile rows, all gate or all up (a half-block has >= 16 rows)
+                const int v0 = T::kRowsPerDmaB * gb;
+                const int within = v0 % T::kWaveN;
+                const int src = (v0 / T::kWaveN) * (T::kWaveN / 2) + within % (T::kWaveN / 2);
+                dma_x4(within < T::kWaveN / 2 ? b_rsrc : u_rsrc, ld_voff_b,
+                       src * (int)kb + step * T::kStrideB, st + T::kABytes + 1024 * gb);
+            } else {
+                dma_x4(b_rsrc, ld_voff_b, T::kRowsPerDmaB * gb * (int)kb + step * T::kStrideB,
+                       st + T::kABytes + 1024 * gb);
+            }
         }
     };
 
@@ -222,7 +246,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // hidden behind the whole main loop.  They are older than every operand
     // load, so the first operand wait also covers them.
     const bool want_sx = L.out_kind != kOutI32;
-    const bool has_sw = L.s_w != nullptr, has_bias = L.bias != nullptr;
+    // (SwiGLU reads its two weight-scale vectors in the epilogue instead)
+    const bool has_sw = !GLU && L.s_w != nullptr, has_bias = !GLU && L.bias != nullptr;
     const bool has_post = POST && L.post != 0;
     {
         constexpr int kSeg = (BM + 3 * BN) / 64;
@@ -435,6 +460,99 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // into per-slot 64-bit products
     asm volatile("" : "+v"(y_lane));
     asm volatile("" : "+v"(r_lane));
+
+    // Output of four consecutive columns starting at element offset y_off.
+    auto store4 = [&](int64_t y_off, const float (&t)[4], bool vec, int64_t first_col) {
+        if (kind == kOutF32) {
+            float *y = static_cast<float *>(Yv) + y_off;
+            if (vec) {
+                __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
+            } else {
+                for (int e = 0; e < 4 && first_col + e < N; ++e)
+                    y[e] = t[e];
+            }
+        } else {
+            const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
+            const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
+            uint16_t *y = static_cast<uint16_t *>(Yv) + y_off;
+            if (vec) {
+                __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u *>(y));
+            } else {
+                const unsigned ws[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+                for (int e = 0; e < 4 && first_col + e < N; ++e)
+                    y[e] = (uint16_t)ws[e];
+            }
+        }
+    };
+
+    if constexpr (GLU) {
+        // SwiGLU: lane l owns output column quad l % kOutQuads of its wave
+        // (gate columns at 4q.., up columns at kWaveN/2 + 4q.. of the staged
+        // rows) and rows l / kOutQuads + kGluRowStep * s of each slice.
+        //   g = fl(fl(fl(A_g) * s_x) * s_w_gate) [/ alpha]
+        //   u = fl(fl(fl(A_u) * s_x) * s_w_up) [/ alpha]
+        //   y = fl(silu(g) * u),  silu(g) = fl(g * fl(1 / fl(1 + exp(-g))))
+        // with exp correctly rounded; one output cast.
+        constexpr int kOutQuads = T::kWaveN / 8;
+        constexpr int kGluSlots = 16 * kOutQuads / 64;
+        constexpr int kGluRowStep = 64 / kOutQuads;
+        static_assert(64 % kOutQuads == 0 && kGluSlots >= 1, "");
+        const int cqo = lane % kOutQuads, rg0 = lane / kOutQuads;
+        const int64_t oc = n0o + wn * (T::kWaveN / 2) + 4 * cqo;
+        const bool oc_any = oc < N;
+        const bool oc_full = (L.vec_store != 0) && (oc + 4 <= N);
+        float swg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, swu[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (oc + e < N) {
+                if (L.s_w)
+                    swg[e] = L.s_w[oc + e];
+                if (L.s_w_up)
+                    swu[e] = L.s_w_up[oc + e];
+            }
+        }
+        int64_t g_lane = (m0 + wm * T::kWaveM + rg0) * ldy + oc;
+        asm volatile("" : "+v"(g_lane));
+#pragma unroll
+        for (int i = 0; i < T::kTM; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
+#pragma unroll
+            for (int sl = 0; sl < kGluSlots; ++sl) {
+                const int rr = rg0 + kGluRowStep * sl;
+                const v4i ag = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cqo);
+                const v4i au = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + T::kWaveN / 2 + 4 * cqo);
+                const int rl = wm * T::kWaveM + i * 16 + rr;
+                if (rl >= rows_valid || !oc_any)
+                    continue;
+                const float sxr = sx_lds[rl];
+                float t[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float g = (float)ag[e];
+                    g = g * sxr;
+                    g = g * swg[e];
+                    float u = (float)au[e];
+                    u = u * sxr;
+                    u = u * swu[e];
+                    if constexpr (DIV) {
+                        g = __fdiv_rn(g, alpha);
+                        u = __fdiv_rn(u, alpha);
+                    }
+                    const float sg = __fdiv_rn(1.0f, 1.0f + convrot_expf::expf_cr(-g));
+                    const float a = g * sg;
+                    t[e] = a * u;
+                }
+                store4(g_lane + (int64_t)(i * 16 + kGluRowStep * sl) * ldy, t, oc_full, oc);
+            }
+        }
+        return;
+    }
+
 #pragma unroll
     for (int i = 0; i < T::kTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -548,26 +666,35 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     int total = 0;
     for (int d = 0; d < p.n_lin; ++d) {
-        p.lin[d].tiles_n = (int)((p.lin[d].N + BN - 1) / BN);
+        // a SwiGLU pair spends two tile columns per output column
+        const int64_t cols = p.lin[d].glu ? 2 * p.lin[d].N : p.lin[d].N;
+        p.lin[d].tiles_n = (int)((cols + BN - 1) / BN);
         p.lin[d].tile_begin = total;
         total += tiles_m * p.lin[d].tiles_n;
     }
     if (total == 0)
         return hipSuccess;
-    // the unscale division and the gated residual are compiled in only when
-    // some linear needs them
-    bool div = false, post = false;
+    // the unscale division and the epilogue extras are compiled in only when
+    // some linear needs them (a SwiGLU problem holds SwiGLU pairs only)
+    bool div = false, post = false, glu = false;
     for (int d = 0; d < p.n_lin; ++d) {
         div = div || p.lin[d].alpha != 1.0f;
         post = post || p.lin[d].post != 0;
+        glu = glu || p.lin[d].glu != 0;
     }
-#define CONVROT_GEMM(D, P)                                                                       \
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, D, WB, P>), dim3(total),         \
+#define CONVROT_GEMM(D, E)                                                                       \
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, STAGES, D, WB, E>), dim3(total),         \
                        dim3(T::kThreads), 0, stream, p, tiles_m, total)
+    if constexpr (WB == 8) {
+        if (glu) {
+            if (div) CONVROT_GEMM(true, kEpiGlu); else CONVROT_GEMM(false, kEpiGlu);
+            return hipGetLastError();
+        }
+    }
     if (post) {
-        if (div) CONVROT_GEMM(true, true); else CONVROT_GEMM(false, true);
+        if (div) CONVROT_GEMM(true, kEpiPost); else CONVROT_GEMM(false, kEpiPost);
     } else {
-        if (div) CONVROT_GEMM(true, false); else CONVROT_GEMM(false, false);
+        if (div) CONVROT_GEMM(true, kEpiPlain); else CONVROT_GEMM(false, kEpiPlain);
     }
 #undef CONVROT_GEMM
     return hipGetLastError();
@@ -590,7 +717,7 @@ hipError_t launch_gemm(GemmProblem p, hipStream_t stream)
     // workgroup, and no faster otherwise.
     int64_t big = 0;
     for (int d = 0; d < p.n_lin; ++d)
-        big += ((p.M + 255) / 256) * ((p.lin[d].N + 255) / 256);
+        big += ((p.M + 255) / 256) * (((p.lin[d].glu ? 2 : 1) * p.lin[d].N + 255) / 256);
     constexpr int64_t kBigTiles = 160;
     if (p.w_bits == 4) {
         if (big >= kBigTiles)

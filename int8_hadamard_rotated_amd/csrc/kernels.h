@@ -57,6 +57,9 @@ struct GemmLinear {
     const void *residual;// post: [M][ld_res] in the output dtype (may equal Y exactly)
     int64_t ld_res;
     int res_vec;         // post: residual row starts allow 4-element vector loads
+    int glu;             // 1: SwiGLU pair, Y = silu(gate reconstruction) * up reconstruction
+    const int8_t *Qw_up; // glu: up weights [N][K] (Qw holds the gate weights)
+    const float *s_w_up; // glu: [N] or null
     int tiles_n;         // filled by the launcher
     int tile_begin;      // filled by the launcher: first linear tile index
 };

@@ -53,7 +53,8 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
 def max_rel_err(got: np.ndarray, want: np.ndarray) -> float:
     """max |got - want| / max(|want|, 1e-6 * rms(want)), in binary64."""
     g, w = got.astype(np.float64), want.astype(np.float64)
-    floor = 1e-6 * float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    # (an all-zero reference still gives a finite ratio)
+    floor = max(1e-6 * float(np.sqrt(np.mean(w * w))), np.finfo(np.float64).tiny) if w.size else 0.0
     return float(np.max(np.abs(g - w) / np.maximum(np.abs(w), floor))) if w.size else 0.0
 
 

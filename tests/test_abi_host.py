@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
         "convrot_packed_bytes", "convrot_quantize_rows", "int8_linear", "convrot_workspace_bytes",
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
-        "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf"])
+        "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf",
+        "int8_swiglu_linear"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -155,6 +156,22 @@ def test_producer_validation(lib):
     pre.kind = 9
     assert f(ctypes.c_void_p(BASE), cr.F32, 8, 256, 256, ctypes.byref(pre), 16, 1, ctypes.byref(d),
              ctypes.c_void_p(BASE + 48 * MB), MB, None) == EUNSUP
+
+
+def test_swiglu_validation(lib):
+    f = lib.int8_swiglu_linear
+    def call(Qx=BASE, sx=BASE + 8 * MB, M=8, K=256, Wg=BASE + 16 * MB, sg=BASE + 24 * MB,
+             Wu=BASE + 40 * MB, su=BASE + 48 * MB, N=32, a=1.0, Y=BASE + 32 * MB, dt=cr.F32):
+        return f(ctypes.c_void_p(Qx), ctypes.c_void_p(sx), M, K, ctypes.c_void_p(Wg), ctypes.c_void_p(sg),
+                 ctypes.c_void_p(Wu), ctypes.c_void_p(su), N, ctypes.c_float(a), ctypes.c_void_p(Y),
+                 dt, N, None)
+    assert call(M=0) == OK
+    assert call(K=100) == EUNSUP
+    assert call(Wu=0) == EINVAL
+    assert call(Wg=BASE + 16 * MB + 4) == EINVAL
+    assert call(Y=BASE + 40 * MB + 64) == EOVL                   # output on the up weights
+    assert call(Y=BASE + 48 * MB) == EOVL                        # ... or the up scales
+    assert call(a=-1.0) == EINVAL
 
 
 def test_expf_validation(lib):

@@ -66,6 +66,7 @@ class Workload:
     rmsnorm: bool = False             # RMSNorm -> Mul(weight) ahead of the Modulate
     rms_eps: float = 1e-6
     glu: int = 0                      # 1 SiLU, 2 Sigmoid: fl(act(X) * up) ahead of the rotation
+    swiglu: bool = False              # the two linears are a SwiGLU pair (gate, up), bias-free
     note: str = ""
 
     @property
@@ -94,6 +95,9 @@ WORKLOADS = {
     "proj_gated": Workload("proj_gated", 4096, 3072, 3072, 256, BF16, BF16, (1.0,), seed=7,
                            gated=True,
                            note="DiT output projection with its gated residual, in place"),
+    "mlp_up_swiglu": Workload("mlp_up_swiglu", 4096, 3072, 12288, 256, BF16, BF16, (1.0, 1.0),
+                              seed=10, swiglu=True,
+                              note="DiT SwiGLU MLP up-projection: gate and up weights, one dual GEMM"),
     "mlp_down_glu": Workload("mlp_down_glu", 4096, 12288, 3072, 256, BF16, BF16, (1.0,), seed=9,
                              glu=1, note="DiT MLP down-projection of silu(gate) * up, fused"),
     "mlp_down": Workload("mlp_down", 16384, 12288, 3072, 256, BF16, BF16, (1.0,), seed=4,
