@@ -45,6 +45,16 @@ constexpr double kOverflow = 0x1.fffffep127 + 0x1p103;   // FLT_MAX + half its u
 
 CONVROT_HD inline double fma_d(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
+// A constant the device keeps in a scalar register pair, so that a binary64
+// multiply-add takes it as an operand instead of rebuilding it per use.
+CONVROT_HD inline double uniform(double c)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm("" : "+s"(c));
+#endif
+    return c;
+}
+
 // 2^k * v for -150 <= k <= 130 as two scalings by powers of two, each exact
 // because every value involved stays a normal binary64 number.
 CONVROT_HD inline double scale2(double v, int k)
@@ -139,24 +149,25 @@ CONVROT_HD inline float expf_cr(float x)
     if (x < -104.0f)
         return 0.0f;
     const double xd = x;
-    const double k = __builtin_rint(xd * kInvLn2);
-    double r = fma_d(-k, kLn2Hi, xd);
-    r = fma_d(-k, kLn2Lo, r);
-    double p = 1.0 / 6227020800.0;                        // 1/13!
-    p = fma_d(p, r, 1.0 / 479001600.0);
-    p = fma_d(p, r, 1.0 / 39916800.0);
-    p = fma_d(p, r, 1.0 / 3628800.0);
-    p = fma_d(p, r, 1.0 / 362880.0);
-    p = fma_d(p, r, 1.0 / 40320.0);
-    p = fma_d(p, r, 1.0 / 5040.0);
-    p = fma_d(p, r, 1.0 / 720.0);
-    p = fma_d(p, r, 1.0 / 120.0);
-    p = fma_d(p, r, 1.0 / 24.0);
-    p = fma_d(p, r, 1.0 / 6.0);
+    const double k = __builtin_rint(xd * uniform(kInvLn2));
+    double r = fma_d(-k, uniform(kLn2Hi), xd);
+    r = fma_d(-k, uniform(kLn2Lo), r);
+    double p = uniform(1.0 / 6227020800.0);               // 1/13!
+    p = fma_d(p, r, uniform(1.0 / 479001600.0));
+    p = fma_d(p, r, uniform(1.0 / 39916800.0));
+    p = fma_d(p, r, uniform(1.0 / 3628800.0));
+    p = fma_d(p, r, uniform(1.0 / 362880.0));
+    p = fma_d(p, r, uniform(1.0 / 40320.0));
+    p = fma_d(p, r, uniform(1.0 / 5040.0));
+    p = fma_d(p, r, uniform(1.0 / 720.0));
+    p = fma_d(p, r, uniform(1.0 / 120.0));
+    p = fma_d(p, r, uniform(1.0 / 24.0));
+    p = fma_d(p, r, uniform(1.0 / 6.0));
     p = fma_d(p, r, 0.5);
     p = fma_d(p, r, 1.0);
     p = fma_d(p, r, 1.0);
-    const double y = scale2(p, (int)k);
+    // |k| <= 150, so 2^k and p * 2^k are normal binary64 numbers: exact
+    const double y = __builtin_ldexp(p, (int)k);
     const float f = (float)y;
     if (y >= 0x1p-126 && y < 0x1.fffffep127) {
         const uint32_t low = (uint32_t)(__builtin_bit_cast(uint64_t, y) & 0x1FFFFFFFu);
