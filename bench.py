@@ -356,6 +356,20 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / args.steps
 
+    def kernel_spread(fn, n=100):
+        """p10 / median / p90 of single launches, each between its own pair of
+        HIP events (the GPU idles for a few microseconds between them)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        return {"launches": n, "p10": round(float(np.percentile(us, 10)), 3),
+                "median": round(float(np.median(us)), 3), "p90": round(float(np.percentile(us, 90)), 3)}
+
     ops = gemm_ops(w, w.n_linears)
     rec = {
         "metric": "int8 linear TOPS + quantize GB/s (fraction of MI355X roofline), M=4096 K=3072",
@@ -391,13 +405,15 @@ def main() -> int:
         rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
                            "us": round(tq * 1e6, 3), "bytes": quantize_bytes(w),
-                           "traffic": measured_traffic("quantize", w.name)}
+                           "traffic": measured_traffic("quantize", w.name),
+                           "single_launch_us": kernel_spread(quantize)}
         rec["roofline"] = {"bound": "mfma", "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS,
                            "unit": "TFLOP/s", "frac": round(g_tops / INT8_PEAK_TOPS, 4),
                            "traffic": measured_traffic("gemm", w.name),
                            "kernel": "gemm_i8 (contraction + fused reconstruction)",
                            "us": round(tg * 1e6, 3),
-                           "note": "int8 ops: one multiply-add counts as 2"}
+                           "note": "int8 ops: one multiply-add counts as 2",
+                           "single_launch_us": kernel_spread(gemm)}
     else:
         rec["roofline"] = None
         rec["quantize"] = None
