@@ -43,7 +43,9 @@
  *   - Device pointers unless stated otherwise; the caller owns all memory.
  *     The library never allocates, frees or retains memory, and never
  *     synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL is
- *     the default stream) in call order.
+ *     the default stream) in call order.  Calls enqueue kernel launches only
+ *     (no memory fills or copies), so they may be captured into a HIP graph;
+ *     a replay reads the buffers' contents at replay time.
  *   - Row-major, last index contiguous.  X is [M][ldx] (elements), W-side
  *     codes Q_w are [N][K], Y is [M][ldy] (elements).
  *   - Arguments are validated on the host before anything is enqueued; on any
