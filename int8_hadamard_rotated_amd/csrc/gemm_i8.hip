@@ -29,6 +29,8 @@
 #include "expf_cr.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace convrot_detail {
 namespace {
 
@@ -191,6 +193,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int64_t n0o = GLU ? (int64_t)tn * (BN / 2) : n0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (lets the compiler resolve which operand a wave's DMA instruction
+    // moves, where the instruction count is a multiple of the wave count)
+    __builtin_assume(wave >= 0 && wave < T::kWaves);
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- global -> LDS by direct buffer loads.  A stage holds the BM rows
@@ -340,15 +345,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     static_assert((S - 2) * T::kLoads < 64, "vmcnt range");
     v4i fa[T::kTM], fb[T::kTN];
     const int ksteps = (int)(K / kBK);
-    auto iteration = [&](int k) {
-        const bool has_next = k + 1 < ksteps;
-        const bool expand = WB == 4 && k + 2 < ksteps;
+    //
+    // Iterations k <= ksteps - S (steady state) have a next step, issue DMA
+    // and leave S - 3 - AH steps in flight at the wait: they run a copy of
+    // the body with those facts fixed at compile time (no per-step branches);
+    // the last S - 1 iterations run the general body.
+    auto iteration = [&](int k, auto steady) {
+        constexpr bool STEADY = decltype(steady)::value;
+        const bool has_next = STEADY || k + 1 < ksteps;
+        const bool expand = WB == 4 && (STEADY || k + 2 < ksteps);
         if (has_next) {
             // steps up to k+1+AH must have landed; k+2+AH .. k+S-2 may stay in flight
-            int younger = ksteps - k - 2 - AH;
-            younger = younger < S - 3 - AH ? younger : S - 3 - AH;
-            younger = younger > 0 ? younger : 0;
-            wait_vmcnt_le<(S - 3 - AH) * T::kLoads>(younger * my_loads);
+            if constexpr (STEADY && T::kDma % T::kWaves == 0) {
+                wait_vmcnt<(S - 3 - AH) * T::kLoads>();      // every wave issues kLoads per step
+            } else {
+                int younger = ksteps - k - 2 - AH;
+                younger = younger < S - 3 - AH ? younger : S - 3 - AH;
+                younger = younger > 0 ? younger : 0;
+                wait_vmcnt_le<(S - 3 - AH) * T::kLoads>(younger * my_loads);
+            }
             __syncthreads();
         }
         v2u pk{0u, 0u};
@@ -357,7 +372,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 pk = read_packed(k + 2);
         }
         const int dma_step = k + S - 1;
-        const bool dma = dma_step < ksteps;
+        const bool dma = STEADY || dma_step < ksteps;
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -404,8 +419,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
     for (int j = 0; j < T::kTN; ++j)
         fb[j] = read_b(0, j);
-    for (int k = 0; k < ksteps; ++k)
-        iteration(k);
+    int k = 0;
+    for (; k + S - 1 < ksteps; ++k)
+        iteration(k, std::integral_constant<bool, true>{});
+    for (; k < ksteps; ++k)
+        iteration(k, std::integral_constant<bool, false>{});
     __syncthreads();
 
     // ---- epilogue.  The MFMA 16x16 result block leaves lane l with column
