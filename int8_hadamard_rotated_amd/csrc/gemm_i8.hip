@@ -479,9 +479,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     asm volatile("" : "+v"(y_lane));
     asm volatile("" : "+v"(r_lane));
 
-    // Output of four consecutive columns starting at element offset y_off.
-    auto store4 = [&](int64_t y_off, const float (&t)[4], bool vec, int64_t first_col) {
-        if (kind == kOutF32) {
+    // Output of four consecutive columns starting at element offset y_off
+    // (KIND: kOutF32 or kOutBF16).
+    auto store4 = [&](auto kind_tag, int64_t y_off, const float (&t)[4], bool vec, int64_t first_col) {
+        if constexpr (decltype(kind_tag)::value == kOutF32) {
             float *y = static_cast<float *>(Yv) + y_off;
             if (vec) {
                 __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
@@ -531,6 +532,68 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         }
         int64_t g_lane = (m0 + wm * T::kWaveM + rg0) * ldy + oc;
         asm volatile("" : "+v"(g_lane));
+        auto glu_epilogue = [&](auto kind_tag, auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+            for (int i = 0; i < T::kTM; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < T::kTN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
+#pragma unroll
+                for (int sl = 0; sl < kGluSlots; ++sl) {
+                    const int rr = rg0 + kGluRowStep * sl;
+                    const v4i ag = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cqo);
+                    const v4i au = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + T::kWaveN / 2 + 4 * cqo);
+                    const int rl = wm * T::kWaveM + i * 16 + rr;
+                    if (!FULL && (rl >= rows_valid || !oc_any))
+                        continue;
+                    const float sxr = sx_lds[rl];
+                    float t[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float g = (float)ag[e];
+                        g = g * sxr;
+                        g = g * swg[e];
+                        float u = (float)au[e];
+                        u = u * sxr;
+                        u = u * swu[e];
+                        if constexpr (DIV) {
+                            g = __fdiv_rn(g, alpha);
+                            u = __fdiv_rn(u, alpha);
+                        }
+                        const float sg = __fdiv_rn(1.0f, 1.0f + convrot_expf::expf_cr(-g));
+                        const float a = g * sg;
+                        t[e] = a * u;
+                    }
+                    store4(kind_tag, g_lane + (int64_t)(i * 16 + kGluRowStep * sl) * ldy, t, FULL || oc_full, oc);
+                }
+            }
+        };
+        // tiles wholly inside Y with vector stores allowed skip every bounds check
+        const bool tile_full = L.vec_store != 0 && n0o + BN / 2 <= N && m0 + BM <= M;
+        if (kind == kOutF32) {
+            if (tile_full)
+                glu_epilogue(std::integral_constant<int, kOutF32>{}, std::true_type{});
+            else
+                glu_epilogue(std::integral_constant<int, kOutF32>{}, std::false_type{});
+        } else {
+            if (tile_full)
+                glu_epilogue(std::integral_constant<int, kOutBF16>{}, std::true_type{});
+            else
+                glu_epilogue(std::integral_constant<int, kOutBF16>{}, std::false_type{});
+        }
+        return;
+    }
+
+    // The plain and gated-residual epilogue, with the output kind and, for
+    // tiles wholly inside Y with vector stores allowed, the absence of bounds
+    // checks fixed at compile time (no per-slot branches on either).
+    auto epilogue = [&](auto kind_tag, auto full_tag) {
+        constexpr int KIND = decltype(kind_tag)::value;
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -538,142 +601,118 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             for (int j = 0; j < T::kTN; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
+                    stage[(row_in + v) * kStageStride + j * 16 + col_in] =
+                        WB == 4 ? (acc[i][j][v] >> 4) : acc[i][j][v];   // 4-bit weights: 16 A
 #pragma unroll
-            for (int sl = 0; sl < kGluSlots; ++sl) {
-                const int rr = rg0 + kGluRowStep * sl;
-                const v4i ag = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cqo);
-                const v4i au = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + T::kWaveN / 2 + 4 * cqo);
-                const int rl = wm * T::kWaveM + i * 16 + rr;
-                if (rl >= rows_valid || !oc_any)
+            for (int sl = 0; sl < kSlots; ++sl) {
+                const int rr = rr0 + kRowStep * sl;
+                const v4i a = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cq);
+                const int rl = wm * T::kWaveM + i * 16 + rr;        // row within the tile
+                if (!FULL && (rl >= rows_valid || !col_any))
                     continue;
-                const float sxr = sx_lds[rl];
-                float t[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float g = (float)ag[e];
-                    g = g * sxr;
-                    g = g * swg[e];
-                    float u = (float)au[e];
-                    u = u * sxr;
-                    u = u * swu[e];
-                    if constexpr (DIV) {
-                        g = __fdiv_rn(g, alpha);
-                        u = __fdiv_rn(u, alpha);
-                    }
-                    const float sg = __fdiv_rn(1.0f, 1.0f + convrot_expf::expf_cr(-g));
-                    const float a = g * sg;
-                    t[e] = a * u;
-                }
-                store4(g_lane + (int64_t)(i * 16 + kGluRowStep * sl) * ldy, t, oc_full, oc);
-            }
-        }
-        return;
-    }
-
-#pragma unroll
-    for (int i = 0; i < T::kTM; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < T::kTN; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                stage[(row_in + v) * kStageStride + j * 16 + col_in] =
-                    WB == 4 ? (acc[i][j][v] >> 4) : acc[i][j][v];   // 4-bit weights: 16 A
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-            const int rr = rr0 + kRowStep * sl;
-            const v4i a = *reinterpret_cast<const v4i *>(stage + rr * kStageStride + 4 * cq);
-            const int rl = wm * T::kWaveM + i * 16 + rr;        // row within the tile
-            if (rl >= rows_valid || !col_any)
-                continue;
-            const int dr = i * 16 + kRowStep * sl;              // rows below the lane's first
-            const int64_t y_off = y_lane + (int64_t)dr * ldy;
-            if (kind == kOutI32) {
-                int32_t *y = static_cast<int32_t *>(Yv) + y_off;
-                if (full) {
-                    *reinterpret_cast<v4i *>(y) = a;
-                } else {
-                    for (int e = 0; e < 4 && o + e < N; ++e)
-                        y[e] = a[e];
-                }
-                continue;
-            }
-            const float sxr = sx_lds[rl];
-            float t[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float x = (float)a[e];
-                x = x * sxr;
-                x = x * sw[e];
-                if constexpr (DIV)
-                    x = __fdiv_rn(x, alpha);
-                x = x + bo[e];
-                t[e] = x;
-            }
-            if constexpr (POST) {
-                if (has_post) {
-                    // fl(fl(fl(y * scale) * gate) + residual), the residual in
-                    // the output dtype (bf16 widened exactly)
-                    float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if (kind == kOutF32) {
-                        const float *rp = static_cast<const float *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
-                        if (res_full) {
-                            const v4f q = *reinterpret_cast<const v4f *>(rp);
-                            rv[0] = q.x; rv[1] = q.y; rv[2] = q.z; rv[3] = q.w;
-                        } else {
-                            for (int e = 0; e < 4 && o + e < N; ++e)
-                                rv[e] = rp[e];
-                        }
+                const int dr = i * 16 + kRowStep * sl;              // rows below the lane's first
+                const int64_t y_off = y_lane + (int64_t)dr * ldy;
+                if constexpr (KIND == kOutI32) {
+                    int32_t *y = static_cast<int32_t *>(Yv) + y_off;
+                    if (FULL || full) {
+                        *reinterpret_cast<v4i *>(y) = a;
                     } else {
-                        const uint16_t *rp = static_cast<const uint16_t *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
-                        unsigned h[4] = {0u, 0u, 0u, 0u};
-                        if (res_full) {
-                            const v2u q = *reinterpret_cast<const v2u *>(rp);
-                            h[0] = q.x & 0xFFFFu; h[1] = q.x >> 16; h[2] = q.y & 0xFFFFu; h[3] = q.y >> 16;
-                        } else {
-                            for (int e = 0; e < 4 && o + e < N; ++e)
-                                h[e] = rp[e];
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            rv[e] = __builtin_bit_cast(float, h[e] << 16);
+                        for (int e = 0; e < 4 && o + e < N; ++e)
+                            y[e] = a[e];
                     }
+                    continue;
+                } else {
+                    const float sxr = sx_lds[rl];
+                    float t[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float x = t[e];
-                        if (post_scale != 1.0f)
-                            x = x * post_scale;
-                        x = x * gt[e];
-                        t[e] = x + rv[e];
+                        float x = (float)a[e];
+                        x = x * sxr;
+                        x = x * sw[e];
+                        if constexpr (DIV)
+                            x = __fdiv_rn(x, alpha);
+                        x = x + bo[e];
+                        t[e] = x;
+                    }
+                    if constexpr (POST) {
+                        if (has_post) {
+                            // fl(fl(fl(y * scale) * gate) + residual), the residual in
+                            // the output dtype (bf16 widened exactly)
+                            float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                            if constexpr (KIND == kOutF32) {
+                                const float *rp = static_cast<const float *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
+                                if (res_full) {
+                                    const v4f q = *reinterpret_cast<const v4f *>(rp);
+                                    rv[0] = q.x; rv[1] = q.y; rv[2] = q.z; rv[3] = q.w;
+                                } else {
+                                    for (int e = 0; e < 4 && o + e < N; ++e)
+                                        rv[e] = rp[e];
+                                }
+                            } else {
+                                const uint16_t *rp = static_cast<const uint16_t *>(L.residual) + r_lane + (int64_t)dr * L.ld_res;
+                                unsigned h[4] = {0u, 0u, 0u, 0u};
+                                if (res_full) {
+                                    const v2u q = *reinterpret_cast<const v2u *>(rp);
+                                    h[0] = q.x & 0xFFFFu; h[1] = q.x >> 16; h[2] = q.y & 0xFFFFu; h[3] = q.y >> 16;
+                                } else {
+                                    for (int e = 0; e < 4 && o + e < N; ++e)
+                                        h[e] = rp[e];
+                                }
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    rv[e] = __builtin_bit_cast(float, h[e] << 16);
+                            }
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x = t[e];
+                                if (post_scale != 1.0f)
+                                    x = x * post_scale;
+                                x = x * gt[e];
+                                t[e] = x + rv[e];
+                            }
+                        }
+                    }
+                    if constexpr (KIND == kOutF32) {
+                        float *y = static_cast<float *>(Yv) + y_off;
+                        if (FULL || full) {
+                            __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
+                        } else {
+                            for (int e = 0; e < 4 && o + e < N; ++e)
+                                y[e] = t[e];
+                        }
+                    } else {
+                        // Round to nearest even (the hardware conversion, finite
+                        // inputs).  Both halves are taken from the packed words with
+                        // integer operations: extracting the high element of a bf16
+                        // vector is miscompiled by this toolchain.
+                        const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
+                        const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
+                        uint16_t *y = static_cast<uint16_t *>(Yv) + y_off;
+                        if (FULL || full) {
+                            __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u *>(y));
+                        } else {
+                            const unsigned ws[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+                            for (int e = 0; e < 4 && o + e < N; ++e)
+                                y[e] = (uint16_t)ws[e];
+                        }
                     }
                 }
             }
-            if (kind == kOutF32) {
-                float *y = static_cast<float *>(Yv) + y_off;
-                if (full) {
-                    __builtin_nontemporal_store(v4f{t[0], t[1], t[2], t[3]}, reinterpret_cast<v4f *>(y));
-                } else {
-                    for (int e = 0; e < 4 && o + e < N; ++e)
-                        y[e] = t[e];
-                }
-            } else {
-                // Round to nearest even (the hardware conversion, finite
-                // inputs).  Both halves are taken from the packed words with
-                // integer operations: extracting the high element of a bf16
-                // vector is miscompiled by this toolchain.
-                const unsigned w0 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[0], t[1]}, v2bf));
-                const unsigned w1 = __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{t[2], t[3]}, v2bf));
-                uint16_t *y = static_cast<uint16_t *>(Yv) + y_off;
-                if (full) {
-                    __builtin_nontemporal_store(v2u{w0, w1}, reinterpret_cast<v2u *>(y));
-                } else {
-                    const unsigned ws[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
-                    for (int e = 0; e < 4 && o + e < N; ++e)
-                        y[e] = (uint16_t)ws[e];
-                }
-            }
         }
+    };
+    const bool tile_full = L.vec_store != 0 && n0 + BN <= N && m0 + BM <= M;
+    if (kind == kOutBF16) {
+        if (tile_full)
+            epilogue(std::integral_constant<int, kOutBF16>{}, std::true_type{});
+        else
+            epilogue(std::integral_constant<int, kOutBF16>{}, std::false_type{});
+    } else if (kind == kOutF32) {
+        if (tile_full)
+            epilogue(std::integral_constant<int, kOutF32>{}, std::true_type{});
+        else
+            epilogue(std::integral_constant<int, kOutF32>{}, std::false_type{});
+    } else {
+        epilogue(std::integral_constant<int, kOutI32>{}, std::false_type{});
     }
 }
 
