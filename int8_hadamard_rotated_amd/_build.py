@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -27,17 +28,46 @@ FLAGS = [
 ]
 
 
+# the compiler's per-kernel resource report, checked below
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def register_spills(remarks: str) -> list[str]:
+    """Kernels whose resource report shows VGPRs or SGPRs spilled to scratch.
+
+    A spill in these kernels is a performance fault (the GEMM's accumulators
+    and the quantizer's row data are sized to stay in registers), so the build
+    refuses it rather than ship a silently slower library."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+([VS])GPRs Spill: (\d+)", line)
+        if m and int(m.group(2)) > 0:
+            bad.append(f"{name}: {m.group(1)}GPRs spill {m.group(2)}")
+    return bad
+
+
 def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source into one shared library (always recompiles)."""
+    """Compile every source into one shared library (always recompiles) and
+    refuse a build in which any kernel spills registers."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = output + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *RESOURCE_REMARKS, *(extra or []), *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
-    if verbose and res.stderr:
-        sys.stderr.write(res.stderr)
+    spills = register_spills(res.stderr)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels spill registers:\n  " + "\n  ".join(spills))
+    if verbose:
+        warnings = [l for l in res.stderr.splitlines() if "warning" in l]
+        if warnings:
+            sys.stderr.write("\n".join(warnings) + "\n")
     os.replace(tmp, output)
     return output
 

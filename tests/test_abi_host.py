@@ -314,3 +314,19 @@ def test_fused_validation(lib):
     assert f(*args(BASE + 128 * MB, BASE + 256 * MB, need - 16)) == EWS
     assert f(*args(BASE + 64 * MB, BASE + 256 * MB, need)) == EOVL          # Y on the weights
     assert f(*args(BASE + 256 * MB, BASE + 256 * MB, need)) == EOVL         # Y on the workspace
+
+
+def test_build_refuses_register_spills():
+    """The build reads hipcc's per-kernel resource report and refuses any
+    kernel that spills registers (checked here on report text of both kinds)."""
+    from int8_hadamard_rotated_amd import _build
+    clean = ("x.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]\n"
+             "x.hip:1:1: remark:     VGPRs: 103 [-Rpass-analysis=kernel-resource-usage]\n"
+             "x.hip:1:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+             "x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    spilling = clean + ("x.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]\n"
+                        "x.hip:9:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+                        "x.hip:9:1: remark:     VGPRs Spill: 12 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert _build.register_spills(clean) == []
+    assert _build.register_spills(spilling) == ["kern_b: VGPRs spill 12"]
+    assert "-Rpass-analysis=kernel-resource-usage" in _build.RESOURCE_REMARKS
