@@ -254,6 +254,13 @@ __device__ __forceinline__ void weight8(float (&v)[8], const float *__restrict__
         v[p] = v[p] * wv[p];
 }
 
+// LDS index of element e of the gated activation's staged rows: 4 floats of
+// padding after every 256 (an 8-element piece never straddles a boundary).
+__device__ __forceinline__ int act_index(int e) { return e + (e >> 8) * 4; }
+
+// Dynamic LDS bytes of that staging for `elems` elements.
+inline size_t act_stage_bytes(int64_t elems) { return (size_t)(elems + (elems >> 8) * 4 + 8) * 4; }
+
 // The gated activation on one value: sigmoid(g) = fl(1 / fl(1 + exp(-g)))
 // with exp correctly rounded; SiLU is fl(g * sigmoid(g)).  Division by IEEE
 // rule (the toolchain's default single-precision division is correctly
@@ -339,9 +346,16 @@ __device__ __forceinline__ void modulate8(float (&v)[8], const float *__restrict
 // (two waves per SIMD), so that the row data, the block sums or the exp's
 // binary64 temporaries fit in registers.
 //
-// A gated activation (ACT != 0) reads the second input up with the same
-// lane layout as X and replaces each value by fl(act(x) * u) right after
-// widening.
+// A gated activation (ACT != 0) first computes fl(act(x) * u) over the
+// workgroup's rows in a plain layout: thread t takes the 8-element pieces
+// t, t + T, t + 2T, ... (T threads) of the rows laid end to end, with
+// coalesced 16- or 32-byte loads of x and up, in a loop that is not unrolled,
+// so that only one piece's exps are in flight per thread and the kernel
+// keeps few registers.  The binary32 results go to LDS (act_stage; 4 floats
+// of padding after every 256, so that the quads of a wave, whose spans are
+// 256 elements apart, read distinct banks), and the quad layout then reads
+// its values from there.  Same arithmetic per element as the other producers'
+// direct path; it only changes where the values wait.
 template <typename XT, int G, int NC, bool SCALED, int MOD, bool RMS, int ACT>
 __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_kernel(
     const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
@@ -355,6 +369,7 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
     __shared__ unsigned row_max[256];
     __shared__ float norm_part[RMS ? 256 * kBlocks : 1];
     __shared__ float norm_r[RMS ? 256 : 1];
+    extern __shared__ __attribute__((aligned(16))) float act_stage[];
 
     const int tid = threadIdx.x;
     const int quad = tid >> 2;
@@ -364,31 +379,57 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
     static_assert(ACT == 0 || (MOD == 0 && !RMS), "one producer at a time");
     const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
     const int64_t span0 = (int64_t)q_in_row * (32 * NC);
+    // With a gated activation the workgroup may have more threads than the
+    // quad layout uses (4 per quad): the extra ones only share the
+    // activation pass, then wait at the barriers.
+    const bool worker = tid < 4 * quads_per_row * rows_per_wg;
     // A quad never straddles rows, so this branch is uniform per quad and the
     // DPP exchanges below only read lanes that take the same path.
-    const bool live = row < M;
+    const bool live = worker && row < M;
 
     if (tid < rows_per_wg)
         row_max[tid] = 0u;
     __syncthreads();
 
     float v[NC][8];
-    if (live) {
+    if constexpr (ACT != 0) {
+        const int n_threads = (int)blockDim.x;
+        const int row_len = (int)K;
+        const int elems = rows_per_wg * row_len;
+#pragma unroll 1
+        for (int e = 8 * tid; e < elems; e += 8 * n_threads) {   // element of the rows laid end to end
+            const int rl = e / row_len;
+            const int col = e - rl * row_len;
+            const int64_t grow = (int64_t)blockIdx.x * rows_per_wg + rl;
+            if (grow < M) {
+                float g[8], u[8];
+                load8(X + grow * ldx + col, g);
+                load8(up + grow * ld_up + col, u);
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    g[p] = gated_act<ACT>(g[p]) * u[p];
+                float *dst = act_stage + act_index(e);
+                *reinterpret_cast<v4f *>(dst) = v4f{g[0], g[1], g[2], g[3]};
+                *reinterpret_cast<v4f *>(dst + 4) = v4f{g[4], g[5], g[6], g[7]};
+            }
+        }
+        __syncthreads();
+        if (live) {
+            const int base = row_local * row_len + (int)span0;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float *src = act_stage + act_index(base + chunk_offset(j0, j1, c));
+                const v4f a = *reinterpret_cast<const v4f *>(src);
+                const v4f b = *reinterpret_cast<const v4f *>(src + 4);
+                v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
+                v[c][4] = b.x; v[c][5] = b.y; v[c][6] = b.z; v[c][7] = b.w;
+            }
+        }
+    } else if (live) {
         const XT *xr = X + row * ldx + span0;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             load8(xr + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1), v[c]);
-        if constexpr (ACT != 0) {
-            const XT *ur = up + row * ld_up + span0;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                float u[8];
-                load8(ur + chunk_offset(j0, j1, c), u);
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    v[c][p] = gated_act<ACT>(v[c][p]) * u[p];
-            }
-        }
     }
     if constexpr (RMS) {
         const int row_blocks = quads_per_row * kBlocks;
@@ -445,7 +486,7 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
             atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
     }
     __syncthreads();
-    if (row >= M_pad)
+    if (!worker || row >= M_pad)
         return;
 
     int8_t *qr = Q + row * K + span0;
@@ -656,7 +697,11 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
         rows = kMaxThreads / (4 * qr) > 0 ? kMaxThreads / (4 * qr) : 1;
     while (4 * qr * rows * 2 <= 256)
         rows *= 2;
-    const int threads = 4 * qr * rows;
+    int threads = 4 * qr * rows;
+    // the gated activation doubles the threads of its activation pass where
+    // the launch bounds allow (the quad layout keeps 4 * qr * rows of them)
+    if (ACT != 0 && 2 * threads <= kMaxThreads)
+        threads *= 2;
     const int64_t blocks = (m_pad + rows - 1) / rows;
     int8_t *Q = static_cast<int8_t *>(packed);
     float *S = reinterpret_cast<float *>(Q + m_pad * K);
@@ -667,14 +712,25 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                                              S, m_pad, qr, rows, stream);
     }
     const XT *up = static_cast<const XT *>(pre.up);
+    // the gated activation stages the workgroup's rows in LDS (at most 512
+    // threads of 64 elements: 130 KB)
+    const size_t lds = ACT != 0 ? act_stage_bytes((int64_t)rows * K) : 0;
+    if (lds > 64 * 1024) {
+        // beyond the default dynamic LDS limit of a launch
+        const void *fn = alpha != 1.0f
+                             ? reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT>)
+                             : reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT>);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return;   // the launch below is then not made; the caller sees the error
+    }
     if (alpha != 1.0f)
         hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT>), dim3((unsigned)blocks),
-                           dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
+                           dim3(threads), lds, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
                            alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
                            qr, rows);
     else
         hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT>), dim3((unsigned)blocks),
-                           dim3(threads), 0, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
+                           dim3(threads), lds, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
                            alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
                            qr, rows);
 }
