@@ -47,6 +47,24 @@ def test_modulated_quantize_bit_exact(orc, dtype):
                                       f"M={M} K={K} G={G} {dtype} shift={shift is not None} a={alpha}")
 
 
+
+def test_modulated_vectors_at_lds_limit(orc):
+    """The workgroup quantizer stages the Modulate scale and shift in LDS when
+    both fit in 48 KB: K = 6144 is the largest such row (both paths of the
+    launch rule meet there), K = 6208 the smallest row past it.  Six rows, so
+    that the last workgroup also holds pad rows."""
+    rng = np.random.default_rng(54)
+    for dtype in (workloads.F32, workloads.BF16):
+        for K, G in ((6144, 256), (6208, 64)):
+            X = workloads.gaussian_activations(rng, 6, K, 0.01, 30.0, dtype)
+            sc, sh = workloads.modulation(rng, K)
+            for shift in (sh, None):
+                say("modulated quantize at the LDS limit", K, G, dtype, shift is not None)
+                got = host(cr.convrot_quantize_rows_pre(
+                    dev_x(X), cr.Modulate(dev(sc), None if shift is None else dev(shift)), G))
+                assert_bits_equal(got, want_packed(orc, X, G, 1.0, sc, shift),
+                                  f"K={K} G={G} {dtype} shift={shift is not None}")
+
 def test_modulated_quantize_workload_and_stride(orc):
     """mlp_up's producer-fused pass in full, and strided rows."""
     w = workloads.WORKLOADS["mlp_up_mod"]

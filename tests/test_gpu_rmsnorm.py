@@ -65,6 +65,23 @@ def test_rmsnorm_quantize_bit_exact(orc, dtype):
                               f"M={M} K={K} G={G2} {dtype} alpha 0.3")
 
 
+
+def test_rmsnorm_vectors_at_lds_limit(orc):
+    """With a Modulate, the RMSNorm weight is staged in LDS beside the scale
+    and shift when all three fit in 48 KB: K = 4096 is the largest such row,
+    K = 4160 the smallest past it."""
+    rng = np.random.default_rng(62)
+    for dtype in (workloads.F32, workloads.BF16):
+        for K, G in ((4096, 256), (4160, 64)):
+            X = workloads.gaussian_activations(rng, 6, K, 0.01, 30.0, dtype)
+            w = workloads.norm_weight(rng, K)
+            sc, sh = workloads.modulation(rng, K)
+            for (ww, s1, s2) in ((w, sc, sh), (None, sc, sh)):
+                say("rmsnorm quantize at the LDS limit", K, G, dtype, ww is not None)
+                got = host(cr.convrot_quantize_rows_pre(dev_x(X), pre(1e-6, ww, s1, s2), G))
+                assert_bits_equal(got, want_packed(orc, X, G, 1.0, 1e-6, ww, s1, s2),
+                                  f"K={K} G={G} {dtype} w={ww is not None}")
+
 def test_rmsnorm_special_rows(orc):
     """Zero rows (eps > 0), constant rows of +-2^k (eps = 0), magnitudes up to
     2^40 and down to 2^-40, and a single outlier."""
