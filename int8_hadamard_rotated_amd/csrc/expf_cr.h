@@ -8,8 +8,13 @@
 //
 // Method: argument reduction x = k ln2 + r with a three-part ln2 (its first
 // part short enough that k * part is exact), |r| <= ln2 / 2, then
-//   fast path: the Taylor series of exp(r) to degree 13 in binary64 with
-//     fused multiply-adds (relative error below 2^-51), scaled by 2^k; its
+//   fast path: a degree-10 polynomial in binary64 with fused multiply-adds,
+//     scaled by 2^k.  The polynomial is the Chebyshev series of exp on
+//     [-0.3466, 0.3466] truncated after degree 10 (its coefficients are twice
+//     the modified Bessel values I_j(0.3466), I_0 once), rewritten in powers of
+//     r and rounded to binary64: relative error 2^-51.3 before evaluation,
+//     below 2^-50 with the evaluation's rounding, so within the 2^-49 window
+//     below (the Taylor series needs degree 13 for the same bound).  Its
 //     binary32 rounding is returned unless the binary64 value lies within
 //     2^-49 (relative) of a binary32 rounding boundary: for binary32-normal
 //     results, unless the 29 bits of the binary64 significand below binary32
@@ -152,19 +157,17 @@ CONVROT_HD inline float expf_cr(float x)
     const double k = __builtin_rint(xd * uniform(kInvLn2));
     double r = fma_d(-k, uniform(kLn2Hi), xd);
     r = fma_d(-k, uniform(kLn2Lo), r);
-    double p = uniform(1.0 / 6227020800.0);               // 1/13!
-    p = fma_d(p, r, uniform(1.0 / 479001600.0));
-    p = fma_d(p, r, uniform(1.0 / 39916800.0));
-    p = fma_d(p, r, uniform(1.0 / 3628800.0));
-    p = fma_d(p, r, uniform(1.0 / 362880.0));
-    p = fma_d(p, r, uniform(1.0 / 40320.0));
-    p = fma_d(p, r, uniform(1.0 / 5040.0));
-    p = fma_d(p, r, uniform(1.0 / 720.0));
-    p = fma_d(p, r, uniform(1.0 / 120.0));
-    p = fma_d(p, r, uniform(1.0 / 24.0));
-    p = fma_d(p, r, uniform(1.0 / 6.0));
-    p = fma_d(p, r, 0.5);
-    p = fma_d(p, r, 1.0);
+    // the degree-10 polynomial of the fast path (see the header comment)
+    double p = uniform(0x1.28b40e50912c4p-22);
+    p = fma_d(p, r, uniform(0x1.72fafc8b35748p-19));
+    p = fma_d(p, r, uniform(0x1.a01991a2e8693p-16));
+    p = fma_d(p, r, uniform(0x1.a01978baa91ffp-13));
+    p = fma_d(p, r, uniform(0x1.6c16c187ff82fp-10));
+    p = fma_d(p, r, uniform(0x1.1111112dda5a8p-7));
+    p = fma_d(p, r, uniform(0x1.555555554f0bdp-5));
+    p = fma_d(p, r, uniform(0x1.555555554b73ap-3));
+    p = fma_d(p, r, uniform(0x1.0000000000011p-1));
+    p = fma_d(p, r, uniform(0x1.000000000001ep+0));
     p = fma_d(p, r, 1.0);
     // |k| <= 150, so 2^k and p * 2^k are normal binary64 numbers: exact
     const double y = __builtin_ldexp(p, (int)k);
