@@ -77,6 +77,12 @@ __device__ __forceinline__ float quad_swap(float x)
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+template <int CTRL>
+__device__ __forceinline__ unsigned quad_swap_u(unsigned x)
+{
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
 // H4 on four in-register values.
 __device__ __forceinline__ void h4_local(float &x0, float &x1, float &x2, float &x3)
 {
@@ -604,9 +610,18 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
     const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
     if (q_in_row == 0 && (tid & 3) == 0)
         S[row] = __fdiv_rn(m, 127.0f);
+    // Chunks c and c + 1 of the lane pair (j0 = 0, 1) cover 32 consecutive
+    // bytes: [0, 8) and [16, 24) in lane 0, [8, 16) and [24, 32) in lane 1.
+    // One exchange across the pair leaves [0, 16) in lane 0 and [16, 32) in
+    // lane 1, so that every lane stores 16 bytes and a quad 64 contiguous ones.
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-        *reinterpret_cast<v2u *>(qr + chunk_offset(j0, j1, c)) = encode8(v[c], inv);
+    for (int c = 0; c < NC; c += 2) {
+        const v2u e0 = encode8(v[c], inv), e1 = encode8(v[c + 1], inv);
+        const v2u send = j0 ? e0 : e1;
+        const v2u recv{quad_swap_u<kQuadPermXor1>(send.x), quad_swap_u<kQuadPermXor1>(send.y)};
+        const v2u lo = j0 ? recv : e0, hi = j0 ? e1 : recv;
+        *reinterpret_cast<v4u *>(qr + chunk_offset(0, j1, c) + 16 * j0) = v4u{lo.x, lo.y, hi.x, hi.y};
+    }
 }
 
 // ---- binary32 inputs: the same arithmetic with the row data staged in LDS.
