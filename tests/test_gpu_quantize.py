@@ -7,7 +7,7 @@ import int8_hadamard_rotated_amd as cr
 import oracle
 import pins
 import workloads
-from gpu_util import THREADS, assert_bits_equal, dev_x, host, say
+from gpu_util import THREADS, assert_bits_equal, dev, dev_x, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +34,10 @@ def test_workload_packed_bit_exact(orc, name):
         assert_bits_equal(got, want, f"{name} packed (alpha={alpha})")
 
 
-# K = 4096 and 8192 fill a 256-thread workgroup (4 waves) of the staged binary32 kernel.
-# bf16 rows with K % 256 == 0 whose rows fill 1, 2 or 3 passes of 16 quads run
-# whole rows per wave: 16 rows per wave (K = 256, 768), 8 (512, 1536), 4 (3072),
-# 2 (6144) and 1 (4096, 8192, 12288); K = 1280 and 65536 do not fit and take the
-# workgroup kernel.
+# Rows of 1 to 256 quad spans in both kernels: binary32 rows whose workgroups
+# need at most 256 threads take the LDS-staged kernel (K = 4096 and 8192 fill
+# its 4 waves), longer binary32 rows and every bf16 row the workgroup kernel;
+# spans of 64, 128 and 256 elements (K % 256 != 0 takes the shorter ones).
 EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (13, 512), (17, 768),
                (33, 1280), (11, 1536), (129, 3072), (9, 4096), (3, 6144), (6, 8192), (7, 12288),
                (2, 65536)]
@@ -57,6 +56,25 @@ def test_edge_shapes(orc, G, dtype):
             assert_bits_equal(gpu_packed(X, G, alpha), orc.quantize_rows(X, G, alpha).raw,
                               f"M={M} K={K} G={G} {dtype} alpha={alpha}")
 
+
+
+def test_wave_stores_with_pad_rows(orc):
+    """Passes of at least 8192 waves in whole waves store their codes through
+    LDS, 1 KB per store instruction, with every lane storing pieces of other
+    quads.  131 073 bf16 rows of 256: 2049 workgroups of 64 rows (8196
+    waves), three pad rows, and 60 rows past the packed tensor in the last
+    workgroup, which must not be written."""
+    rng = np.random.default_rng(107)
+    M, K = 131073, 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    nb = cr.convrot_packed_bytes(M, K)
+    Xd = dev_x(X)
+    packed = dev(np.full(nb + 4096, 0x5A, dtype=np.uint8))
+    say("wave stores", M, K)
+    cr.convrot_quantize_rows(Xd, 256, packed=packed)
+    got = host(packed)
+    assert_bits_equal(got[:nb], orc.quantize_rows(X, 256).raw, "wave-store packed")
+    assert np.all(got[nb:] == 0x5A), "bytes past the packed tensor were written"
 
 def test_row_stride(orc):
     rng = np.random.default_rng(7)
