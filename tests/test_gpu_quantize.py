@@ -58,22 +58,29 @@ def test_edge_shapes(orc, G, dtype):
 
 
 
-def test_wave_stores_with_pad_rows(orc):
+# (rows, K, dtype, G): 131 073 bf16 rows of 256 make 2049 workgroups of 64
+# rows (8196 waves) with three pad rows and 60 rows past the packed tensor in
+# the last workgroup; 1025 binary32 rows of 32 768 take the workgroup kernel
+# (512 threads, 8224 waves); 26 215 bf16 rows of 320 use spans of 64 elements
+# (16 rows per workgroup, 8195 waves).
+WAVE_STORE_SHAPES = [(131073, 256, workloads.BF16, 256), (1025, 32768, workloads.F32, 256),
+                     (26215, 320, workloads.BF16, 64)]
+
+
+@pytest.mark.parametrize("M,K,dtype,G", WAVE_STORE_SHAPES)
+def test_wave_stores_with_pad_rows(orc, M, K, dtype, G):
     """Passes of at least 8192 waves in whole waves store their codes through
     LDS, 1 KB per store instruction, with every lane storing pieces of other
-    quads.  131 073 bf16 rows of 256: 2049 workgroups of 64 rows (8196
-    waves), three pad rows, and 60 rows past the packed tensor in the last
-    workgroup, which must not be written."""
+    quads.  Bytes past the packed tensor must stay untouched."""
     rng = np.random.default_rng(107)
-    M, K = 131073, 256
-    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, dtype)
     nb = cr.convrot_packed_bytes(M, K)
     Xd = dev_x(X)
     packed = dev(np.full(nb + 4096, 0x5A, dtype=np.uint8))
-    say("wave stores", M, K)
-    cr.convrot_quantize_rows(Xd, 256, packed=packed)
+    say("wave stores", M, K, dtype, G)
+    cr.convrot_quantize_rows(Xd, G, packed=packed)
     got = host(packed)
-    assert_bits_equal(got[:nb], orc.quantize_rows(X, 256).raw, "wave-store packed")
+    assert_bits_equal(got[:nb], orc.quantize_rows(X, G).raw, f"wave-store packed M={M} K={K} {dtype}")
     assert np.all(got[nb:] == 0x5A), "bytes past the packed tensor were written"
 
 def test_row_stride(orc):
