@@ -319,6 +319,21 @@ __device__ __forceinline__ v2u encode8(const float (&v)[8], float inv)
     return out;
 }
 
+// Codes of chunks c and c + 1 of the two lanes of a pair (j0 = 0, 1): they
+// cover 32 consecutive bytes, [0, 8) and [16, 24) in lane 0, [8, 16) and
+// [24, 32) in lane 1.  One exchange across the pair returns [0, 16) to lane 0
+// and [16, 32) to lane 1, so that every lane stores 16 bytes at
+// chunk_offset(0, j1, c) + 16 j0 and a quad 64 contiguous ones.  Both lanes of
+// the pair must be active.
+__device__ __forceinline__ v4u encode_pair16(const float (&a)[8], const float (&b)[8], float inv, int j0)
+{
+    const v2u e0 = encode8(a, inv), e1 = encode8(b, inv);
+    const v2u send = j0 ? e0 : e1;
+    const v2u recv{quad_swap_u<kQuadPermXor1>(send.x), quad_swap_u<kQuadPermXor1>(send.y)};
+    const v2u lo = j0 ? recv : e0, hi = j0 ? e1 : recv;
+    return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
 // Workgroup quad index -> (row within the workgroup, quad within the row).
 // Without a producer quads are row-major.  With the Modulate producer they
 // are column-major, so that the quads of one wave that read the same columns
@@ -618,13 +633,8 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
                 if (q_in_row == 0 && (tid & 3) == 0)
                     S[row] = __fdiv_rn(m, 127.0f);
 #pragma unroll
-                for (int c = 0; c < NC; c += 2) {
-                    const v2u e0 = encode8(v[c], inv), e1 = encode8(v[c + 1], inv);
-                    const v2u send = j0 ? e0 : e1;
-                    const v2u recv{quad_swap_u<kQuadPermXor1>(send.x), quad_swap_u<kQuadPermXor1>(send.y)};
-                    const v2u lo = j0 ? recv : e0, hi = j0 ? e1 : recv;
-                    *reinterpret_cast<v4u *>(sq + chunk_offset(0, j1, c) + 16 * j0) = v4u{lo.x, lo.y, hi.x, hi.y};
-                }
+                for (int c = 0; c < NC; c += 2)
+                    *reinterpret_cast<v4u *>(sq + chunk_offset(0, j1, c) + 16 * j0) = encode_pair16(v[c], v[c + 1], inv, j0);
             }
         }
         const int64_t wave_q0 = (int64_t)blockIdx.x * rows_per_wg * quads_per_row + 16 * wave;
@@ -659,18 +669,9 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
     const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
     if (q_in_row == 0 && (tid & 3) == 0)
         S[row] = __fdiv_rn(m, 127.0f);
-    // Chunks c and c + 1 of the lane pair (j0 = 0, 1) cover 32 consecutive
-    // bytes: [0, 8) and [16, 24) in lane 0, [8, 16) and [24, 32) in lane 1.
-    // One exchange across the pair leaves [0, 16) in lane 0 and [16, 32) in
-    // lane 1, so that every lane stores 16 bytes and a quad 64 contiguous ones.
 #pragma unroll
-    for (int c = 0; c < NC; c += 2) {
-        const v2u e0 = encode8(v[c], inv), e1 = encode8(v[c + 1], inv);
-        const v2u send = j0 ? e0 : e1;
-        const v2u recv{quad_swap_u<kQuadPermXor1>(send.x), quad_swap_u<kQuadPermXor1>(send.y)};
-        const v2u lo = j0 ? recv : e0, hi = j0 ? e1 : recv;
-        *reinterpret_cast<v4u *>(qr + chunk_offset(0, j1, c) + 16 * j0) = v4u{lo.x, lo.y, hi.x, hi.y};
-    }
+    for (int c = 0; c < NC; c += 2)
+        *reinterpret_cast<v4u *>(qr + chunk_offset(0, j1, c) + 16 * j0) = encode_pair16(v[c], v[c + 1], inv, j0);
 }
 
 // ---- binary32 inputs: the same arithmetic with the row data staged in LDS.
