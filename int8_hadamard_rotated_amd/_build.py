@@ -5,10 +5,12 @@ import os
 import re
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libconvrot.so")
+OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["convrot_api.cpp", "quantize.hip", "gemm_i8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -17,7 +19,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # binary32 results must match the oracle bit for bit: no contraction, no
     # fast-math, IEEE denormals kept (the HIP default for gfx950)
     "-ffp-contract=off",
@@ -50,24 +51,38 @@ def register_spills(remarks: str) -> list[str]:
     return bad
 
 
+def _compile(src: str, extra: list[str]) -> tuple[str, subprocess.CompletedProcess]:
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *RESOURCE_REMARKS, *extra, "-c", src, "-o", obj]
+    return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+
 def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source into one shared library (always recompiles) and
-    refuse a build in which any kernel spills registers."""
+    """Compile every source (in parallel, always recompiling) and link one
+    shared library; refuse a build in which any kernel spills registers."""
+    os.makedirs(OBJDIR, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as pool:
+        results = list(pool.map(lambda s: _compile(s, list(extra or [])), srcs))
+    remarks = ""
+    for src, (obj, res) in zip(srcs, results):
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed ({res.returncode}) on {src}")
+        remarks += res.stderr
+    spills = register_spills(remarks)
+    if spills:
+        raise RuntimeError("kernels spill registers:\n  " + "\n  ".join(spills))
+    if verbose:
+        warnings = [l for l in remarks.splitlines() if "warning" in l]
+        if warnings:
+            sys.stderr.write("\n".join(warnings) + "\n")
     tmp = output + ".tmp"
-    cmd = [HIPCC, *FLAGS, *RESOURCE_REMARKS, *(extra or []), *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
-    spills = register_spills(res.stderr)
-    if spills:
-        os.remove(tmp)
-        raise RuntimeError("kernels spill registers:\n  " + "\n  ".join(spills))
-    if verbose:
-        warnings = [l for l in res.stderr.splitlines() if "warning" in l]
-        if warnings:
-            sys.stderr.write("\n".join(warnings) + "\n")
+        raise RuntimeError(f"link failed ({res.returncode}): {' '.join(cmd)}")
     os.replace(tmp, output)
     return output
 

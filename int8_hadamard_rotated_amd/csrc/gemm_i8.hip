@@ -436,7 +436,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // memory system absorbs at full rate; 32-byte row pieces per instruction
     // measured at well under half of it.  The staging region is private to
     // the wave and LDS operations of one wave complete in order, so no
-    // barrier separates writing and reading it.
+    // workgroup barrier separates writing and reading it, only a wave-scope
+    // fence that keeps the compiler's order (wave_lds_sync).
     constexpr int kStageStride = T::kWaveN + 4;                 // int32 per staged row
     constexpr int kColQuads = T::kWaveN / 4;
     constexpr int kSlots = 16 * kColQuads / 64;
@@ -542,6 +543,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         stage[(row_in + v) * kStageStride + j * 16 + col_in] = acc[i][j][v];
+                wave_lds_sync();
 #pragma unroll
                 for (int sl = 0; sl < kGluSlots; ++sl) {
                     const int rr = rg0 + kGluRowStep * sl;
@@ -603,6 +605,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 for (int v = 0; v < 4; ++v)
                     stage[(row_in + v) * kStageStride + j * 16 + col_in] =
                         WB == 4 ? (acc[i][j][v] >> 4) : acc[i][j][v];   // 4-bit weights: 16 A
+            wave_lds_sync();
 #pragma unroll
             for (int sl = 0; sl < kSlots; ++sl) {
                 const int rr = rr0 + kRowStep * sl;

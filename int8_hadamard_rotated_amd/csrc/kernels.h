@@ -7,6 +7,17 @@
 
 namespace convrot_detail {
 
+// Orders a wave's earlier LDS writes before its later LDS reads, where lanes
+// read what other lanes of the same wave wrote (wave-private staging regions).
+// The hardware completes one wave's LDS operations in order; the fences keep
+// the compiler from moving a read above the writes it depends on.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------- quantize
 // Largest row (in elements) the quantizer handles for a given K: one
 // workgroup per group of rows, at most 256 quads of 4 lanes per row (128 with

@@ -637,6 +637,7 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
                     *reinterpret_cast<v4u *>(sq + chunk_offset(0, j1, c) + 16 * j0) = encode_pair16(v[c], v[c + 1], inv, j0);
             }
         }
+        wave_lds_sync();   // lanes store pieces other lanes staged
         const int64_t wave_q0 = (int64_t)blockIdx.x * rows_per_wg * quads_per_row + 16 * wave;
         const int64_t q_total = M_pad * quads_per_row;
         const int wg_quads = quads_per_row * rows_per_wg;
@@ -683,7 +684,8 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
 // The pieces go to a wave-private LDS region and each lane reads back its own
 // chunks; the codes take the same route in reverse, so stores are also 1 KB
 // per instruction.  LDS operations of one wave complete in order, so the
-// region needs no barrier.  Odd quads store their pieces with the slot index
+// region needs no workgroup barrier, only a wave-scope fence that keeps the
+// compiler's order (wave_lds_sync).  Odd quads store their pieces with the slot index
 // XOR-ed by one (codes: by 4 * (quad % 4)) so that the lanes of one read
 // instruction spread over distinct LDS banks.
 template <int G, int NC, bool SCALED, int MOD>
@@ -805,6 +807,7 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
             }
         }
     }
+    wave_lds_sync();   // lanes store pieces other lanes staged
 #pragma unroll
     for (int i = 0; i < kStoresPerLane; ++i) {
         const int p = 64 * i + lane;                            // wave code piece
@@ -825,7 +828,7 @@ template <int NC>
 constexpr size_t kStagedWaveBytes = 16 * 32 * NC * 4;
 
 template <int G, int NC, int MOD>
-void launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
+hipError_t launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                    int8_t *Q, float *S, int64_t m_pad, int qr, int rows, hipStream_t stream)
 {
     const int threads = 4 * qr * rows;
@@ -837,6 +840,7 @@ void launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, float alph
     else
         hipLaunchKernelGGL((quantize_rows_staged<G, NC, false, MOD>), dim3((unsigned)blocks), dim3(threads), lds,
                            stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows);
+    return hipGetLastError();
 }
 
 int gcd_int(int a, int b)
@@ -850,7 +854,7 @@ int gcd_int(int a, int b)
 }
 
 template <typename XT, int G, int NC, int MOD, bool RMS, int ACT>
-void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
+hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                   void *packed, hipStream_t stream)
 {
     const int64_t m_pad = (M + 3) / 4 * 4;
@@ -892,15 +896,19 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
     const size_t lds = ACT != 0 ? act_stage_bytes((int64_t)rows * K)
                        : stage_vec ? vec_bytes
                        : wave_store ? (size_t)(threads / 64) * 16 * 32 * NC : 0;
-    auto go = [&](auto ps) {
+    // the kernel's static LDS: row maxima, and RMSNorm's block sums and factors
+    constexpr size_t kStaticLds = 4 * 256 + (RMS ? 4 * 256 * (NC / 2) + 4 * 256 : 8);
+    auto go = [&](auto ps) -> hipError_t {
         constexpr bool PS = decltype(ps)::value;
-        if (lds > 64 * 1024) {
-            // beyond the default dynamic LDS limit of a launch
+        if (lds + kStaticLds > 64 * 1024) {
+            // beyond the default LDS limit of a launch: raise the kernel's
+            // dynamic maximum first, and make no launch if that fails
             const void *fn =
                 alpha != 1.0f ? reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT, PS>)
                               : reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT, PS>);
-            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-                return;   // the launch below is then not made; the caller sees the error
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess)
+                return e;
         }
         if (alpha != 1.0f)
             hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT, PS>), dim3((unsigned)blocks),
@@ -912,65 +920,63 @@ void launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                                dim3(threads), lds, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
                                alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
                                qr, rows, wave_store);
+        return hipGetLastError();
     };
     if constexpr (ACT == 0 && MOD != 0) {
         if (stage_vec)
             return go(std::true_type{});
     }
-    go(std::false_type{});
+    return go(std::false_type{});
 }
 
 template <typename XT, int NC, int MOD, bool RMS, int ACT>
-void launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
-               const PreOp &pre, void *packed, hipStream_t stream)
+hipError_t launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                     const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
-    case 4: launch_typed<XT, 4, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 16: launch_typed<XT, 16, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
-    case 64: launch_typed<XT, 64, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream); break;
+    case 4: return launch_typed<XT, 4, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+    case 16: return launch_typed<XT, 16, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+    case 64: return launch_typed<XT, 64, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
     default:
         if constexpr (NC == 8)
-            launch_typed<XT, 256, 8, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
-        break;
+            return launch_typed<XT, 256, 8, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+        return hipErrorInvalidValue;   // not reached: the API admits G = 256 only with K % 256 == 0
     }
 }
 
 template <typename XT, int MOD, bool RMS, int ACT>
-void launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
-                  const PreOp &pre, void *packed, hipStream_t stream)
+hipError_t launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                        const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (K % 256 == 0)
-        launch_nc<XT, 8, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else if (K % 128 == 0)
-        launch_nc<XT, 4, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else
-        launch_nc<XT, 2, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_nc<XT, 8, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (K % 128 == 0)
+        return launch_nc<XT, 4, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_nc<XT, 2, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT, bool RMS>
-void launch_mod(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
-                const PreOp &pre, void *packed, hipStream_t stream)
+hipError_t launch_mod(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                      const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (pre.scale && pre.shift)
-        launch_dtype<XT, 2, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else if (pre.scale)
-        launch_dtype<XT, 1, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else
-        launch_dtype<XT, 0, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_dtype<XT, 2, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (pre.scale)
+        return launch_dtype<XT, 1, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_dtype<XT, 0, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT>
-void launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
-                const PreOp &pre, void *packed, hipStream_t stream)
+hipError_t launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
+                      const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (pre.kind == kPreRmsNormModulate)
-        launch_mod<XT, true>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else if (pre.kind == kPreGatedAct && pre.act == kActSilu)
-        launch_dtype<XT, 0, false, kActSilu>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else if (pre.kind == kPreGatedAct)
-        launch_dtype<XT, 0, false, kActSigmoid>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else
-        launch_mod<XT, false>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_mod<XT, true>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (pre.kind == kPreGatedAct && pre.act == kActSilu)
+        return launch_dtype<XT, 0, false, kActSilu>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (pre.kind == kPreGatedAct)
+        return launch_dtype<XT, 0, false, kActSigmoid>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_mod<XT, false>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 // y may be x (each lane reads its element before writing it).
@@ -1006,10 +1012,8 @@ hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int
                            float alpha, const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (x_dtype == 0)
-        launch_pre<float>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    else
-        launch_pre<uint16_t>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    return hipGetLastError();
+        return launch_pre<float>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_pre<uint16_t>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 }  // namespace convrot_detail

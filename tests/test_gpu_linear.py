@@ -32,8 +32,11 @@ def check_y(got, want, y_dtype, what):
     assert_bits_equal(got, want, what)
 
 
+# Beyond the small and ragged shapes: (4096 + 13) x 3072 x (4096 + 7) is a
+# grid of 289 tiles of 256 x 256 whose 48 K steps run the peeled steady-state
+# loop with an int32 output, ragged in M and N.
 GEMM_SHAPES = [(1, 64, 1), (3, 128, 17), (129, 192, 250), (257, 3072, 300), (64, 12288, 96),
-               (4096 + 13, 128, 4096 + 7)]
+               (4096 + 13, 128, 4096 + 7), (4096 + 13, 3072, 4096 + 7)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
@@ -44,6 +47,24 @@ def test_gemm_i32_bit_exact(orc, M, K, N):
     say("gemm_i32", M, K, N)
     A = host(cr.convrot_int8_gemm_i32(dev(Qx), dev(Qw)))
     assert_bits_equal(A, orc.gemm_i32(Qx, Qw, threads=THREADS), f"A {M}x{K}x{N}")
+
+
+# The contraction at the full size of each workload, in the tile configuration
+# its linear runs (256 x 256 tiles, steady-state loop over every K step);
+# uniform codes over [-127, 127] give larger sums than quantized activations.
+FULL_GEMMS = {"mlp_up": (4096, 3072, 12288), "qkv": (4096, 3072, 3072),
+              "attn": (1024, 3072, 3072), "mlp_down": (16384, 12288, 3072)}
+
+
+@pytest.mark.parametrize("name", sorted(FULL_GEMMS))
+def test_gemm_i32_full_size(orc, name):
+    M, K, N = FULL_GEMMS[name]
+    rng = np.random.default_rng(K + N + 11)
+    Qx = workloads.random_codes(rng, (M, K))
+    Qw = workloads.random_codes(rng, (N, K))
+    say("gemm_i32 full size", name, M, K, N)
+    A = host(cr.convrot_int8_gemm_i32(dev(Qx), dev(Qw)))
+    assert_bits_equal(A, orc.gemm_i32(Qx, Qw, threads=THREADS), f"A {name} {M}x{K}x{N}")
 
 
 def test_gemm_i32_extreme_k(orc):
@@ -81,6 +102,33 @@ def test_int8_linear_bit_exact(orc, y_dtype, M, K, N):
             check_y(host(Y), want, y_dtype, f"Y {M}x{K}x{N} a={alpha} sw={use_sw} b={use_b}")
 
 
+# Grids of at least 160 tiles of 256 x 256 take the 256 x 256 kernels; with an
+# input scale that is not a power of two those carry the unscale division.
+# 2051 x 5125 is 9 x 21 = 189 such tiles; K = 512 gives 8 steps, so the
+# steady-state loop runs as well.
+BIG_GRID = (2051, 512, 5125)
+
+
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+def test_int8_linear_big_grid_unscale(orc, y_dtype):
+    M, K, N = BIG_GRID
+    rng = np.random.default_rng(91 + y_dtype)
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    Qw, sw = orc.weight_prep(W, 256, threads=THREADS)
+    alpha = 0.3
+    p = orc.quantize_rows(X, 256, alpha, threads=THREADS)
+    A = orc.gemm_i32(p.q, Qw, threads=THREADS)
+    want = orc.epilogue(A, p.s, sw, b, alpha, y_dtype, threads=THREADS)
+    say("int8_linear big grid", M, K, N, y_dtype, alpha)
+    Y = cr.int8_linear(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), alpha, y_dtype=y_dtype)
+    check_y(host(Y), want, y_dtype, f"Y {M}x{K}x{N} alpha={alpha}")
+    # and the fused entry, which quantizes with the same alpha on the GPU
+    say("fused big grid", M, K, N, y_dtype, alpha)
+    Yf = cr.convrot_int8_linear(dev_x(X), 256, alpha, dev(Qw), dev(sw), dev(b), y_dtype=y_dtype)
+    check_y(host(Yf), want, y_dtype, f"fused Y {M}x{K}x{N} alpha={alpha}")
+
+
 def test_int8_linear_strided_output(orc):
     """ldy > N, and an output whose rows do not allow vector stores."""
     rng = np.random.default_rng(5)
@@ -102,18 +150,10 @@ def test_int8_linear_strided_output(orc):
         assert np.all(got[:, N:] == -7.0), "wrote past N"
 
 
-def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
-    rows |= {0, M - 1}
-    return np.array(sorted(rows))
-
-
 @pytest.mark.parametrize("name", ["tiny", "attn", "mlp_up", "mlp_down"])
 def test_fused_workload(orc, name):
     """The fused entry at each workload's full size, in the configuration the
-    benchmark runs; Y compared in full where the oracle is quick, else on
-    sampled rows (each row of the layer is independent of the others)."""
+    benchmark runs; every output compared with the oracle."""
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     Qw, sw = orc.weight_prep(inp.W[0], w.G, threads=THREADS)
@@ -121,9 +161,8 @@ def test_fused_workload(orc, name):
     say("fused", name)
     Y = host(cr.convrot_int8_linear(dev_x(inp.X), w.G, 1.0, dev(Qw), dev(sw), dev(inp.b[0]),
                                     y_dtype=yd))
-    rows = np.arange(w.M) if w.M * w.N * w.K <= 2 ** 34 else sample_rows(w.M, 24, w.seed)
-    want = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[0], 1.0, yd, threads=THREADS)
-    check_y(np.ascontiguousarray(Y[rows]), want, yd, f"{name} Y")
+    want = orc.linear(inp.X, w.G, Qw, sw, inp.b[0], 1.0, yd, threads=THREADS)
+    check_y(Y, want, yd, f"{name} Y")
 
 
 def test_shared_qkv(orc):
@@ -139,11 +178,10 @@ def test_shared_qkv(orc):
             for (q, s), b, a in zip(preps, inp.b, w.input_scales)]
     say("shared qkv")
     outs = [host(y) for y in cr.convrot_int8_linear_shared(Xd, w.G, lins)]
-    rows = sample_rows(w.M, 16, 33)
     for j, (y, a) in enumerate(zip(outs, w.input_scales)):
         Qw, sw = preps[j]
-        want = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[j], a, threads=THREADS)
-        check_y(np.ascontiguousarray(y[rows]), want, oracle.F32, f"qkv linear {j}")
+        want = orc.linear(inp.X, w.G, Qw, sw, inp.b[j], a, threads=THREADS)
+        check_y(y, want, oracle.F32, f"qkv linear {j}")
         say("separate", j)
         sep = host(cr.convrot_int8_linear(Xd, w.G, a, lins[j]["Qw"], lins[j]["s_w"],
                                           lins[j]["bias"]))

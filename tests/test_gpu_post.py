@@ -9,7 +9,7 @@ import int8_hadamard_rotated_amd as cr
 import oracle
 import workloads
 from gpu_util import THREADS, dev, dev_x, host, say
-from test_gpu_linear import check_y, sample_rows
+from test_gpu_linear import check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,31 @@ def test_gated_residual_bit_exact(orc, y_dtype):
             check_y(host(Yi), want, y_dtype, f"gated in place {M}x{K}x{N} scale={scale}")
 
 
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+def test_gated_residual_big_grid_unscale(orc, y_dtype):
+    """189 tiles of 256 x 256 (the gated-residual 256 x 256 kernel) with an
+    input scale that is not a power of two (its unscale division), K = 512 so
+    that the steady-state loop runs; in place on the residual."""
+    rng = np.random.default_rng(73 + y_dtype)
+    M, K, N = 2051, 512, 5125
+    alpha = 0.3
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    W, b = workloads.gaussian_weights(rng, N, K)
+    Qw, sw = orc.weight_prep(W, 256, threads=THREADS)
+    p = orc.quantize_rows(X, 256, alpha, threads=THREADS)
+    A = orc.gemm_i32(p.q, Qw, threads=THREADS)
+    gate = (rng.standard_normal(N) * 0.3).astype(np.float32)
+    R = workloads.gaussian_activations(rng, M, N, 0.0, 1.0,
+                                       workloads.F32 if y_dtype == oracle.F32 else workloads.BF16)
+    Yf = orc.epilogue(A, p.s, sw, b, alpha, oracle.F32, threads=THREADS)
+    want = orc.gated_residual(Yf, gate, R, 0.37, y_dtype, threads=THREADS)
+    Yi = dev_x(R) if y_dtype == oracle.BF16 else dev(R)
+    say("gated residual big grid", M, K, N, y_dtype, alpha)
+    cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), alpha,
+                        cr.GatedResidual(dev(gate), Yi, 0.37), Y=Yi)
+    check_y(host(Yi), want, y_dtype, f"gated big grid alpha={alpha}")
+
+
 def test_gated_residual_strided(orc):
     """A residual with a row stride above N and an output with another one."""
     import torch
@@ -73,7 +98,7 @@ def test_gated_residual_strided(orc):
 
 def test_gated_residual_workload(orc):
     """The DiT output projection with its gated residual in place, at full
-    size from a GPU-quantized packed tensor, sampled rows."""
+    size from a GPU-quantized packed tensor, every output compared."""
     w = workloads.WORKLOADS["proj_gated"]
     inp = workloads.make_inputs(w)
     Qw, sw = orc.weight_prep(inp.W[0], w.G, threads=THREADS)
@@ -83,7 +108,6 @@ def test_gated_residual_workload(orc):
     Y = dev_x(inp.residual)
     cr.int8_linear_post(qx, sx, dev(Qw), dev(sw), dev(inp.b[0]), 1.0,
                         cr.GatedResidual(dev(inp.gate), Y), Y=Y, M=w.M)
-    rows = sample_rows(w.M, 24, w.seed)
-    Yf = orc.linear(inp.X[rows], w.G, Qw, sw, inp.b[0], 1.0, oracle.F32, threads=THREADS)
-    want = orc.gated_residual(Yf, inp.gate, inp.residual[rows], 1.0, oracle.BF16, threads=THREADS)
-    check_y(np.ascontiguousarray(host(Y)[rows]), want, oracle.BF16, "proj_gated Y")
+    Yf = orc.linear(inp.X, w.G, Qw, sw, inp.b[0], 1.0, oracle.F32, threads=THREADS)
+    want = orc.gated_residual(Yf, inp.gate, inp.residual, 1.0, oracle.BF16, threads=THREADS)
+    check_y(host(Y), want, oracle.BF16, "proj_gated Y")

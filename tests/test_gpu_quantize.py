@@ -63,8 +63,14 @@ def test_edge_shapes(orc, G, dtype):
 # the last workgroup; 1025 binary32 rows of 32 768 take the workgroup kernel
 # (512 threads, 8224 waves); 26 215 bf16 rows of 320 use spans of 64 elements
 # (16 rows per workgroup, 8195 waves).
+#   43 691 bf16 rows of 384 use spans of 128 elements (3 quads a row, 16 rows
+# and 3 waves per workgroup, 2731 workgroups: 8193 waves, one pad row);
+# 513 bf16 rows of 65 536 take 1024-thread workgroups of one row whose
+# staging fills 64 KB of dynamic LDS on top of the kernel's static LDS
+# (8256 waves, with three pad rows).
 WAVE_STORE_SHAPES = [(131073, 256, workloads.BF16, 256), (1025, 32768, workloads.F32, 256),
-                     (26215, 320, workloads.BF16, 64)]
+                     (26215, 320, workloads.BF16, 64), (43691, 384, workloads.BF16, 64),
+                     (513, 65536, workloads.BF16, 256)]
 
 
 @pytest.mark.parametrize("M,K,dtype,G", WAVE_STORE_SHAPES)

@@ -10,7 +10,7 @@ import int8_hadamard_rotated_amd as cr
 import oracle
 import workloads
 from gpu_util import THREADS, assert_bits_equal, dev, dev_x, host, say
-from test_gpu_linear import check_y, sample_rows
+from test_gpu_linear import check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,28 @@ def test_swiglu_bit_exact(orc, y_dtype, M, K, N):
             check_y(host(Y), want, y_dtype, f"swiglu {M}x{K}x{N} a={alpha} sw={use_sw}")
 
 
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+def test_swiglu_big_grid_unscale(orc, y_dtype):
+    """2051 rows into 2 x 2567 columns is 9 x 21 = 189 tiles of 256 x 256 (the
+    SwiGLU 256 x 256 kernel), with an input scale that is not a power of two
+    (its unscale division) and K = 512 (8 steps: the steady-state loop runs)."""
+    rng = np.random.default_rng(93 + y_dtype)
+    M, K, N = 2051, 512, 2567
+    alpha = 0.3
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    Wg, _ = workloads.gaussian_weights(rng, N, K)
+    Wu, _ = workloads.gaussian_weights(rng, N, K)
+    Qg, sg = orc.weight_prep(Wg, 256, threads=THREADS)
+    Qu, su = orc.weight_prep(Wu, 256, threads=THREADS)
+    p = orc.quantize_rows(X, 256, alpha, threads=THREADS)
+    want = want_swiglu(orc, orc.gemm_i32(p.q, Qg, threads=THREADS), orc.gemm_i32(p.q, Qu, threads=THREADS),
+                       p.s, sg, su, alpha, y_dtype)
+    say("swiglu big grid", M, K, N, y_dtype, alpha)
+    Y = cr.int8_swiglu_linear(dev(p.q), dev(p.s), dev(Qg), dev(sg), dev(Qu), dev(su), alpha,
+                              y_dtype=y_dtype)
+    check_y(host(Y), want, y_dtype, f"swiglu big grid alpha={alpha}")
+
+
 def test_swiglu_strided_output(orc):
     """ldy > N, and an output whose rows do not allow vector stores."""
     import torch
@@ -77,8 +99,9 @@ def test_swiglu_strided_output(orc):
 
 
 def test_swiglu_workload_then_convrot(orc):
-    """mlp_up_swiglu at full size from a GPU-quantized packed tensor, on sampled
-    rows, then the optional ConvRot of its output (the next linear's input)."""
+    """mlp_up_swiglu at full size from a GPU-quantized packed tensor, every
+    output compared, then the optional ConvRot of its output (the next
+    linear's input)."""
     w = workloads.WORKLOADS["mlp_up_swiglu"]
     inp = workloads.make_inputs(w)
     (Qg, sg), (Qu, su) = [orc.weight_prep(W, w.G, threads=THREADS) for W in inp.W]
@@ -86,18 +109,10 @@ def test_swiglu_workload_then_convrot(orc):
     packed = cr.convrot_quantize_rows(dev_x(inp.X), w.G)
     qx, sx = cr.packed_parts(packed, w.M, w.K)
     Y = cr.int8_swiglu_linear(qx, sx, dev(Qg), dev(sg), dev(Qu), dev(su), y_dtype=oracle.BF16, M=w.M)
-    rows = sample_rows(w.M, 16, 92)
-    p = orc.quantize_rows(inp.X[rows], w.G, threads=THREADS)
+    p = orc.quantize_rows(inp.X, w.G, threads=THREADS)
     want = want_swiglu(orc, orc.gemm_i32(p.q, Qg, threads=THREADS), orc.gemm_i32(p.q, Qu, threads=THREADS),
                        p.s, sg, su, 1.0, oracle.BF16)
-    Yh = host(Y)
-    check_y(np.ascontiguousarray(Yh[rows]), want, oracle.BF16, "mlp_up_swiglu Y")
+    check_y(host(Y), want, oracle.BF16, "mlp_up_swiglu Y")
     say("mlp_up_swiglu convrot of the output")
-    Yrows = torch_rows(Y, rows)
-    got = host(cr.convrot_quantize_rows(Yrows, w.G))
+    got = host(cr.convrot_quantize_rows(Y, w.G))
     assert_bits_equal(got, orc.quantize_rows(want, w.G, threads=THREADS).raw, "convrot of the SwiGLU output")
-
-
-def torch_rows(Y, rows):
-    import torch
-    return Y[torch.from_numpy(rows).to(Y.device)].contiguous()

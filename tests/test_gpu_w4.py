@@ -9,7 +9,7 @@ import int8_hadamard_rotated_amd as cr
 import oracle
 import workloads
 from gpu_util import THREADS, assert_bits_equal, dev, dev_x, host, say
-from test_gpu_linear import check_y, sample_rows
+from test_gpu_linear import check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -69,9 +69,30 @@ def test_int4_linear_bit_exact(orc, y_dtype):
                 check_y(host(Y), want, y_dtype, f"Y {M}x{K}x{N} a={alpha} sw={use_sw} b={use_b}")
 
 
+@pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
+def test_int4_linear_big_grid_unscale(orc, y_dtype):
+    """189 tiles of 256 x 256 (the 4-bit 256 x 256 kernel) with an input scale
+    that is not a power of two (its unscale division); K = 512 is 8 steps, so
+    the 5-stage ring's steady-state loop runs."""
+    rng = np.random.default_rng(63 + y_dtype)
+    M, K, N = 2051, 512, 5125
+    alpha = 0.3
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    W4 = workloads.random_int4_packed(rng, N, K)
+    sw = workloads.random_scales(rng, N, 1e-3, 1e-2)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    p = orc.quantize_rows(X, 256, alpha, threads=THREADS)
+    A = orc.gemm_i32(p.q, orc.unpack_int4(W4, K), threads=THREADS)
+    want = orc.epilogue(A, p.s, sw, b, alpha, y_dtype, threads=THREADS)
+    say("int4_linear big grid", M, K, N, y_dtype, alpha)
+    Y = cr.int4_linear(dev(p.q), dev(p.s), dev(W4), dev(sw), dev(b), alpha, y_dtype=y_dtype)
+    check_y(host(Y), want, y_dtype, f"int4 big grid alpha={alpha}")
+
+
 def test_int4_workload_shares_packed_input(orc):
     """mlp_up with 4-bit weights at full size, from a packed tensor quantized on
-    the GPU (the same packed tensor an INT8 linear would read), sampled rows."""
+    the GPU (the same packed tensor an INT8 linear would read), every output
+    compared."""
     w = workloads.WORKLOADS["mlp_up_w4"]
     inp = workloads.make_inputs(w)
     say("mlp_up_w4")
@@ -79,7 +100,6 @@ def test_int4_workload_shares_packed_input(orc):
     qx, sx = cr.packed_parts(packed, w.M, w.K)
     Y = host(cr.int4_linear(qx, sx, dev(inp.W[0]), dev(inp.s_w[0]), dev(inp.b[0]),
                             y_dtype=oracle.BF16, M=w.M))
-    rows = sample_rows(w.M, 24, w.seed)
-    want = orc.linear(inp.X[rows], w.G, orc.unpack_int4(inp.W[0], w.K), inp.s_w[0], inp.b[0], 1.0,
+    want = orc.linear(inp.X, w.G, orc.unpack_int4(inp.W[0], w.K), inp.s_w[0], inp.b[0], 1.0,
                       oracle.BF16, threads=THREADS)
-    check_y(np.ascontiguousarray(Y[rows]), want, oracle.BF16, "mlp_up_w4 Y")
+    check_y(Y, want, oracle.BF16, "mlp_up_w4 Y")
