@@ -41,8 +41,9 @@
  *
  * Conventions for every entry point:
  *   - Device pointers unless stated otherwise; the caller owns all memory.
- *     The library never allocates, frees or retains memory, and never
- *     synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     The library never allocates, frees or retains memory (the one
+ *     exception is the static buffer of convrot_int8_linear_noalloc, part
+ *     of its code object), and never synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) in call order.  Calls enqueue kernel launches only
  *     (no memory fills or copies), so they may be captured into a HIP graph;
  *     a replay reads the buffers' contents at replay time.
@@ -125,6 +126,23 @@ int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_
                         int group_size, float input_scale, const int8_t *Qw, const float *s_w,
                         const float *bias, int64_t N, void *Y, int y_dtype, int64_t ldy,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* convrot_int8_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  The packed activation tensor goes to a
+ * buffer the library owns: a 64 MiB device array in its code object, one copy
+ * per GPU it runs on, held until the process ends; the call itself allocates
+ * nothing.  Same arguments, semantics and rules as convrot_int8_linear;
+ * CONVROT_EWORKSPACE if convrot_workspace_bytes(M, K, 1) exceeds 64 MiB
+ * (M * K up to about 67 million, e.g. 4096 x 16384).  Every call on one GPU
+ * uses that GPU's one buffer (contents are not preserved; nothing in it needs
+ * to start at zero): calls that can overlap in time on the same GPU, on
+ * different streams or from different threads, race, and must be ordered by
+ * the caller. */
+int convrot_int8_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                int group_size, float input_scale, const int8_t *Qw,
+                                const float *s_w, const float *bias, int64_t N, void *Y,
+                                int y_dtype, int64_t ldy, void *stream);
 
 /* One linear reading a shared input (host-side descriptor). */
 typedef struct {

@@ -153,6 +153,8 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
         "convrot_workspace_bytes": (sz, [i64, i64, i32]),
         "convrot_int8_linear": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp, i32,
                                       i64, vp, sz, vp]),
+        "convrot_int8_linear_noalloc": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp,
+                                              i32, i64, vp]),
         "convrot_int8_linear_shared": (i32, [vp, i32, i64, i64, i64, i32, i32,
                                              ctypes.POINTER(LinearDesc), vp, sz, vp]),
         "convrot_int8_linear_shared_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc),
@@ -400,6 +402,26 @@ def convrot_int8_linear(X, group_size: int, input_scale: float, Qw, s_w=None, bi
                                        N, _ptr(Y), _dtype_code(Y), ldy, _ptr(workspace),
                                        workspace.numel(), _stream(stream, X))
     _check("convrot_int8_linear", rc)
+    return Y
+
+
+def convrot_int8_linear_noalloc(X, group_size: int, input_scale: float, Qw, s_w=None, bias=None,
+                                Y=None, y_dtype: int = F32, stream=None):
+    """convrot_int8_linear with the packed tensor in the library's static
+    device buffer (no workspace argument, no allocation by the call; Y is
+    allocated here only when not given)."""
+    torch = _torch()
+    M, K = X.shape
+    N = Qw.shape[0]
+    ldx = _row_stride(X) if M > 0 else K
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_torch_dtype(y_dtype), device=Qw.device)
+    ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    rc = library().convrot_int8_linear_noalloc(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
+                                               ctypes.c_float(input_scale), _ptr(Qw), _ptr(s_w),
+                                               _ptr(bias), N, _ptr(Y), _dtype_code(Y), ldy,
+                                               _stream(stream, X))
+    _check("convrot_int8_linear_noalloc", rc)
     return Y
 
 

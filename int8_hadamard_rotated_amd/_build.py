@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libconvrot.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["convrot_api.cpp", "quantize.hip", "gemm_i8.hip"]
+SOURCES = ["convrot_api.cpp", "quantize.hip", "gemm_i8.hip", "static_workspace.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

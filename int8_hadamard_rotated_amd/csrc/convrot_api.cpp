@@ -481,10 +481,17 @@ int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t
     return gemm_i32_impl(Qx, Qw, M, K, N, A, stream, 8);
 }
 
-int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                                   const convrot_pre *pre, int group_size, int n,
-                                   const convrot_linear_desc *descs, void *workspace,
-                                   size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The fused entries: validation, one quantization pass per distinct input
+// scale into the workspace, then one grouped GEMM launch per packed tensor.
+// With use_static the workspace is the library's static buffer instead of
+// the caller's (taken only after every other argument has been validated).
+int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                const convrot_pre *pre, int group_size, int n, const convrot_linear_desc *descs,
+                void *workspace, size_t workspace_bytes, bool use_static, void *stream)
 {
     if (n < 1 || n > kMaxLinears || !descs)
         return CONVROT_EINVAL;
@@ -521,8 +528,25 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
     if (M == 0)
         return CONVROT_OK;
 
+    for (int i = 0; i < n; ++i) {
+        for (int k = 0; k < n; ++k) {
+            if (y_hits_weights(chk[i], chk[k]))
+                return CONVROT_EOVERLAP;
+            if (k != i && overlap(chk[i].y, chk[k].y))
+                return CONVROT_EOVERLAP;
+        }
+    }
+
     const int64_t pb = (int64_t)convrot_packed_bytes(M, K);
     const int64_t slot_bytes = round_up(pb, 256);
+    if (use_static) {
+        if (convrot_workspace_bytes(M, K, n_slots) > kStaticWorkspaceBytes)
+            return CONVROT_EWORKSPACE;
+        (void)hipGetLastError();
+        if (static_workspace(&workspace) != hipSuccess)
+            return CONVROT_EHIP;
+        workspace_bytes = kStaticWorkspaceBytes;
+    }
     if (!workspace || workspace_bytes < convrot_workspace_bytes(M, K, n_slots))
         return CONVROT_EWORKSPACE;
     if (!aligned(workspace, 16))
@@ -535,12 +559,6 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
         if (overlap(chk[i].y, ws) || overlap(chk[i].qw, ws) || overlap(chk[i].sw, ws) ||
             overlap(chk[i].b, ws))
             return CONVROT_EOVERLAP;
-        for (int k = 0; k < n; ++k) {
-            if (y_hits_weights(chk[i], chk[k]))
-                return CONVROT_EOVERLAP;
-            if (k != i && overlap(chk[i].y, chk[k].y))
-                return CONVROT_EOVERLAP;
-        }
     }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -578,6 +596,34 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
     return CONVROT_OK;
 }
 
+convrot_linear_desc one_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t N,
+                               float input_scale, void *Y, int y_dtype, int64_t ldy)
+{
+    convrot_linear_desc d;
+    d.Qw = Qw;
+    d.s_w = s_w;
+    d.bias = bias;
+    d.N = N;
+    d.input_scale = input_scale;
+    d.Y = Y;
+    d.y_dtype = y_dtype;
+    d.ldy = ldy;
+    return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const convrot_pre *pre, int group_size, int n,
+                                   const convrot_linear_desc *descs, void *workspace,
+                                   size_t workspace_bytes, void *stream)
+{
+    return shared_impl(X, x_dtype, M, K, ldx, pre, group_size, n, descs, workspace,
+                       workspace_bytes, false, stream);
+}
+
 int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                int group_size, int n, const convrot_linear_desc *descs,
                                void *workspace, size_t workspace_bytes, void *stream)
@@ -591,17 +637,19 @@ int convrot_int8_linear(const void *X, int x_dtype, int64_t M, int64_t K, int64_
                         const float *bias, int64_t N, void *Y, int y_dtype, int64_t ldy,
                         void *workspace, size_t workspace_bytes, void *stream)
 {
-    convrot_linear_desc d;
-    d.Qw = Qw;
-    d.s_w = s_w;
-    d.bias = bias;
-    d.N = N;
-    d.input_scale = input_scale;
-    d.Y = Y;
-    d.y_dtype = y_dtype;
-    d.ldy = ldy;
+    const convrot_linear_desc d = one_linear(Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy);
     return convrot_int8_linear_shared(X, x_dtype, M, K, ldx, group_size, 1, &d, workspace,
                                       workspace_bytes, stream);
+}
+
+int convrot_int8_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                int group_size, float input_scale, const int8_t *Qw,
+                                const float *s_w, const float *bias, int64_t N, void *Y,
+                                int y_dtype, int64_t ldy, void *stream)
+{
+    const convrot_linear_desc d = one_linear(Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy);
+    return shared_impl(X, x_dtype, M, K, ldx, nullptr, group_size, 1, &d, nullptr, 0, true,
+                       stream);
 }
 
 const char *convrot_status_string(int status)

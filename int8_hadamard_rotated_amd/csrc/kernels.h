@@ -88,4 +88,13 @@ struct GemmProblem {
 // Launch one grouped contraction + reconstruction over all linears of `p`.
 hipError_t launch_gemm(GemmProblem p, hipStream_t stream);
 
+// ------------------------------------------------------- static workspace
+// A library-owned device buffer of this many bytes (one per GPU, held until
+// the process ends) for callers that cannot allocate a workspace.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+
+// The current device's copy of that buffer.  Its address is looked up once
+// per device (the first call with that device current); no allocation.
+hipError_t static_workspace(void **ptr);
+
 }  // namespace convrot_detail

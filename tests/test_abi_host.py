@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
         "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf",
-        "int8_swiglu_linear"])
+        "int8_swiglu_linear", "convrot_int8_linear_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -314,6 +314,22 @@ def test_fused_validation(lib):
     assert f(*args(BASE + 128 * MB, BASE + 256 * MB, need - 16)) == EWS
     assert f(*args(BASE + 64 * MB, BASE + 256 * MB, need)) == EOVL          # Y on the weights
     assert f(*args(BASE + 256 * MB, BASE + 256 * MB, need)) == EOVL         # Y on the workspace
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry validates like the fused one and rejects a
+    packed tensor beyond its 64 MiB static buffer, all before any HIP call."""
+    f = lib.convrot_int8_linear_noalloc
+    args = lambda M, K, G=16, Y=BASE + 512 * MB, a=1.0: (
+        ctypes.c_void_p(BASE), cr.F32, M, K, K, G, ctypes.c_float(a),
+        ctypes.c_void_p(BASE + 384 * MB), None, None, 32, ctypes.c_void_p(Y), cr.F32, 32, None)
+    assert cr.convrot_workspace_bytes(8192, 8192, 1) > 64 * MB
+    assert f(*args(8192, 8192)) == EWS                  # beyond the static buffer
+    assert f(*args(8, 256, G=2)) == EUNSUP
+    assert f(*args(8, 256, a=0.0)) == EINVAL
+    assert f(*args(8, 250)) == EUNSUP                   # K % 64
+    assert f(*args(8, 256, Y=BASE + 384 * MB)) == EOVL  # Y on the weights
+    assert f(*args(0, 256)) == OK                       # nothing to do
 
 
 def test_build_refuses_register_spills():
