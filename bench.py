@@ -28,6 +28,7 @@ GPU.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -149,19 +150,48 @@ def to_dev_x(X: np.ndarray, torch):
     return torch.from_numpy(X).to("cuda:0")
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Threads for the oracle: the job's CPU share when the environment states
+    it (OMP_NUM_THREADS), else every core this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dict:
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    the full layer (quantize, int32 contraction, reconstruction) for the first
-    `rows` rows of X against the full weight matrix."""
+    the full layer (producer if any, quantize, int32 contraction,
+    reconstruction) for the first `rows` rows of X against the full weight
+    matrix, each phase timed on its own."""
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     o = oracle.get()
     if w.w_bits == 4:                                                # untimed
         Qw, sw = o.unpack_int4(inp.W[0], w.K), inp.s_w[0]
     else:
         Qw, sw = o.weight_prep(inp.W[0], w.G, threads=threads)
+    Qu = su = None
+    if w.swiglu:
+        Qu, su = o.weight_prep(inp.W[1], w.G, threads=threads)      # untimed
     yd = oracle.BF16 if w.y_dtype == workloads.BF16 else oracle.F32
     X = np.ascontiguousarray(inp.X[:rows])
+    alpha = w.input_scales[0]
+    t = {}
     t0 = time.perf_counter()
     if w.glu:
         X = o.gated_act_rows(X, np.ascontiguousarray(inp.up[:rows]), w.glu, threads=threads)
@@ -169,27 +199,43 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
         X = o.rmsnorm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
     if w.modulate:
         X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
+    t1 = time.perf_counter()
+    pk = o.quantize_rows(X, w.G, alpha, threads=threads)
+    t2 = time.perf_counter()
+    A = o.gemm_i32(pk.q, Qw, threads=threads)
+    Au = o.gemm_i32(pk.q, Qu, threads=threads) if w.swiglu else None
+    t3 = time.perf_counter()
     if w.swiglu:
-        Qu, su = o.weight_prep(inp.W[1], w.G, threads=threads)      # untimed
-        t0 = time.perf_counter()
-        Yg = o.linear(X, w.G, Qw, sw, None, w.input_scales[0], oracle.F32, threads=threads)
-        Yu = o.linear(X, w.G, Qu, su, None, w.input_scales[0], oracle.F32, threads=threads)
+        Yg = o.epilogue(A, pk.s, sw, None, alpha, oracle.F32, threads=threads)
+        Yu = o.epilogue(Au, pk.s, su, None, alpha, oracle.F32, threads=threads)
         o.gated_act_rows(Yg, Yu, oracle.ACT_SILU, threads=threads)
     elif w.gated:
-        Yf = o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], oracle.F32, threads=threads)
+        Yf = o.epilogue(A, pk.s, sw, inp.b[0], alpha, oracle.F32, threads=threads)
         o.gated_residual(Yf, inp.gate, np.ascontiguousarray(inp.residual[:rows]), 1.0, yd,
                          threads=threads)
     else:
-        o.linear(X, w.G, Qw, sw, inp.b[0], w.input_scales[0], yd, threads=threads)
-    dt = time.perf_counter() - t0
-    ops = 2 * rows * w.N * w.K * (2 if w.swiglu else 1)
+        o.epilogue(A, pk.s, sw, inp.b[0], alpha, yd, threads=threads)
+    t4 = time.perf_counter()
+    dt = t4 - t0
+    n_lin = 2 if w.swiglu else 1
+    ops = 2 * rows * w.N * w.K * n_lin
+    esz = 2 if w.x_dtype == workloads.BF16 else 4
+    m_pad = (rows + 3) // 4 * 4
+    q_bytes = rows * w.K * esz + m_pad * w.K + 4 * m_pad
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {w.M} rows of {w.name} ({'gated activation + ' if w.glu else ''}"
                       f"{'RMSNorm + ' if w.rmsnorm else ''}"
                       f"{'modulate + ' if w.modulate else ''}"
                       f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''}"
                       f"{' for the gate and up weights + SwiGLU' if w.swiglu else ''} "
-                      f"against all {w.N}x{w.K} weights), {dt:.2f} s"}
+                      f"against all {w.N}x{w.K} weights), {dt:.2f} s",
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
+            "threads_note": "OpenMP threads = OMP_NUM_THREADS when set (the job's CPU share), "
+                            "else the cores this process may run on",
+            "phases_s": {"producer": round(t1 - t0, 4), "quantize": round(t2 - t1, 4),
+                         "gemm_i32": round(t3 - t2, 4), "reconstruction": round(t4 - t3, 4)},
+            "quantize_gbs": round(q_bytes / (t2 - t1) / 1e9, 3),
+            "gemm_gops": round(ops / (t3 - t2) / 1e9, 3)}
 
 
 def main() -> int:
@@ -209,6 +255,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of X in the CPU oracle sample (0: all of them, one whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the MFMA-rate probe (the contraction's power-limited ceiling)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, pass a float32 tensor of this many MiB three times "
                          "through torch.neg (a plain copy kernel of known size that calibrates "
@@ -247,114 +295,130 @@ def main() -> int:
         Wd = torch.from_numpy(W).to(dev)
         packed = cr.convrot_quantize_rows(Wd, w.G)
         Qw, sw = cr.packed_parts(packed, w.N, w.K)
-        lins.append(dict(Qw=Qw[: w.N], s_w=sw[: w.N], bias=torch.from_numpy(b).to(dev),
-                         input_scale=a))
-        del Wd
+        lins.append(dict(Qw=Qw[: w.N].contiguous(), s_w=sw[: w.N].contiguous(),
+                         bias=torch.from_numpy(b).to(dev), input_scale=a))
+        del Wd, packed
     torch.cuda.synchronize()
 
     yd = cr.BF16 if w.y_dtype == workloads.BF16 else cr.F32
     ybytes = 2 if yd == cr.BF16 else 4
     shared = w.n_linears > 1 and not w.swiglu
-    n_packed = len(set(w.input_scales))
+    scales = sorted(set(w.input_scales), key=w.input_scales.index)   # one pass per distinct scale
+    n_packed = len(scales)
+    w_bytes = sum(l["Qw"].numel() + 8 * w.N for l in lins)
     set_bytes = (inp.X.nbytes * (2 if w.glu else 1) + cr.convrot_workspace_bytes(w.M, w.K, n_packed)
-                 + w.n_linears * w.M * w.N * ybytes)
+                 + w.n_linears * w.M * w.N * ybytes + w_bytes)
     n_sets = args.sets or max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
+    # Every input set has its own activations, packed tensors, outputs and a
+    # copy of the weights (same values), so that nothing a step reads is
+    # still in the 256 MiB Infinity Cache from the step before.
     sets = []
-    ups = []                       # the gated activation's second input, per set
     for s in range(n_sets):
         extra = inp if s == 0 else workloads.make_inputs(w, seed=w.seed + 1000 * s)
-        X = extra.X
-        if w.glu:
-            ups.append(to_dev_x(extra.up, torch))
-        Xd = to_dev_x(X, torch)
+        Xd = to_dev_x(extra.X, torch)
+        up = to_dev_x(extra.up, torch) if w.glu else None
         ws = torch.empty(cr.convrot_workspace_bytes(w.M, w.K, n_packed), dtype=torch.uint8,
                          device=dev)
         Ys = [torch.empty((w.M, w.N), dtype=torch.bfloat16 if yd == cr.BF16 else torch.float32,
                           device=dev) for _ in range(w.n_linears)]
         if w.gated:                  # the output starts as the residual (updated in place)
             Ys[0].copy_(to_dev_x(inp.residual, torch))
-        sets.append((Xd, ws, Ys))
+        ls = lins if s == 0 else [dict(l, Qw=l["Qw"].clone(), s_w=l["s_w"].clone(),
+                                       bias=l["bias"].clone()) for l in lins]
+        slot = cr.convrot_workspace_bytes(w.M, w.K, 1)
+        views = [cr.packed_parts(ws[k * slot:(k + 1) * slot], w.M, w.K) for k in range(n_packed)]
+        sets.append(dict(X=Xd, up=up, ws=ws, Y=Ys, lins=ls, views=views))
+    torch.cuda.synchronize()
 
     mod = (cr.Modulate(torch.from_numpy(inp.mod_scale).to(dev), torch.from_numpy(inp.mod_shift).to(dev))
            if w.modulate else None)
     if w.rmsnorm:
         mod = cr.RMSNormModulate(w.rms_eps, torch.from_numpy(inp.norm_weight).to(dev),
                                  mod.scale if mod else None, mod.shift if mod else None)
-
-    def quantize(i):
-        Xd, ws, Ys = sets[i % n_sets]
-        if w.glu:
-            cr.convrot_quantize_rows_pre(Xd, cr.GatedAct(ups[i % n_sets], w.glu), w.G,
-                                         lins[0]["input_scale"], packed=ws)
-        elif mod is not None:
-            cr.convrot_quantize_rows_pre(Xd, mod, w.G, lins[0]["input_scale"], packed=ws)
-        else:
-            cr.convrot_quantize_rows(Xd, w.G, lins[0]["input_scale"], packed=ws)
-
     gate = torch.from_numpy(inp.gate).to(dev) if w.gated else None
+    slot = cr.convrot_workspace_bytes(w.M, w.K, 1)
 
-    def gemm(i):
-        Xd, ws, Ys = sets[i % n_sets]
-        l = lins[0]
-        qx, sx = views[i % n_sets]
+    def quantize(i, k=0):
+        S = sets[i % n_sets]
+        ws = S["ws"][k * slot:(k + 1) * slot]
+        if w.glu:
+            cr.convrot_quantize_rows_pre(S["X"], cr.GatedAct(S["up"], w.glu), w.G, scales[k], packed=ws)
+        elif mod is not None:
+            cr.convrot_quantize_rows_pre(S["X"], mod, w.G, scales[k], packed=ws)
+        else:
+            cr.convrot_quantize_rows(S["X"], w.G, scales[k], packed=ws)
+
+    def gemm(i, k=0):
+        """The GEMM launch of packed tensor k: every linear whose input scale
+        is scales[k] (one grouped launch when there are several)."""
+        S = sets[i % n_sets]
+        qx, sx = S["views"][k]
+        ls = [dict(l, Y=Y) for l, Y in zip(S["lins"], S["Y"]) if l["input_scale"] == scales[k]]
+        l = ls[0]
         if w.gated:
             cr.int8_linear_post(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"],
-                                cr.GatedResidual(gate, Ys[0]), Y=Ys[0], M=w.M)
-            return
-        if w.swiglu:
-            u = lins[1]
+                                cr.GatedResidual(gate, l["Y"]), Y=l["Y"], M=w.M)
+        elif w.swiglu:
+            u = dict(S["lins"][1], Y=S["Y"][1])
             cr.int8_swiglu_linear(qx, sx, l["Qw"], l["s_w"], u["Qw"], u["s_w"], l["input_scale"],
-                                  Y=Ys[0], M=w.M)
-            return
-        lin_fn = cr.int4_linear if w.w_bits == 4 else cr.int8_linear
-        lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=Ys[0], M=w.M)
+                                  Y=l["Y"], M=w.M)
+        elif len(ls) > 1:
+            cr.int8_linear_grouped(qx, sx, ls, M=w.M)
+        else:
+            lin_fn = cr.int4_linear if w.w_bits == 4 else cr.int8_linear
+            lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=l["Y"], M=w.M)
 
     def step(i):
-        if shared:
-            Xd, ws, Ys = sets[i % n_sets]
-            cr.convrot_int8_linear_shared_pre(
-                Xd, mod, w.G, [dict(l, Y=Y) for l, Y in zip(lins, Ys)], workspace=ws)
-        else:
-            quantize(i)
-            gemm(i)
+        # one quantize pass per distinct input scale, then one GEMM launch per
+        # packed tensor (the launches of the shared entry, without folding a
+        # power-of-two scale into the alpha = 1 pass)
+        for k in range(n_packed):
+            quantize(i, k)
+        for k in range(n_packed):
+            gemm(i, k)
 
-    views = [cr.packed_parts(ws, w.M, w.K) for _, ws, _ in sets]
-    t_warm = time.perf_counter()
-    for i in range(args.warmup):
-        step(i)
-    warm_steps = args.warmup
-    torch.cuda.synchronize()
-    while (time.perf_counter() - t_warm) * 1e3 < args.warmup_ms:
-        for _ in range(16):
-            step(warm_steps)
-            warm_steps += 1
-        torch.cuda.synchronize()
+    def step_folded(i):
+        S = sets[i % n_sets]
+        cr.convrot_int8_linear_shared_pre(
+            S["X"], mod, w.G, [dict(l, Y=Y) for l, Y in zip(S["lins"], S["Y"])], workspace=S["ws"])
 
-    # timed region: K whole steps, HIP events only at its two ends (an event
-    # recorded between kernels leaves the GPU idle for a few microseconds)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+
+    def warm(fn):
+        t_warm = time.perf_counter()
+        for i in range(args.warmup):
+            fn(i)
+        n = args.warmup
+        torch.cuda.synchronize()
+        while (time.perf_counter() - t_warm) * 1e3 < args.warmup_ms:
+            for _ in range(16):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return n
+
+    def timed(fn, n):
+        """Wall time and HIP-event time of n calls (events only at the two ends:
+        an event recorded between kernels leaves the GPU idle a few us)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+    warm_steps = warm(step)
+    wall, ev = timed(step, args.steps)
     ms_per_step = wall * 1e3 / args.steps
-    ev_step_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    ev_step_us = ev * 1e6 / args.steps
 
     def kernel_us(fn):
         """Average duration of one kernel: K launches of it back to back (same
         input rotation as the steps) between two HIP events on its stream."""
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / args.steps
+        return timed(fn, args.steps)[1] * 1e6 / args.steps
 
     def kernel_spread(fn, n=100):
         """p10 / median / p90 of single launches, each between its own pair of
@@ -394,29 +458,80 @@ def main() -> int:
                                + (", Modulate producer fused" if w.modulate else "")
                                + (", gated residual in place" if w.gated else ""),
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,
-                   "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets},
+                   "y_dtype": w.y_dtype, "linears": w.n_linears, "input_sets": n_sets,
+                   "cold": "every set has its own X, packed tensors, Y and weight copy; "
+                           f"{n_sets} sets of {set_bytes / 2**20:.0f} MiB rotate past the "
+                           "256 MiB Infinity Cache"},
         "step_us_events": round(ev_step_us, 3),
     }
-    if not shared:
-        tq = kernel_us(quantize) * 1e-6
-        tg = kernel_us(gemm) * 1e-6
-        q_gbs = quantize_bytes(w) / tq / 1e9
-        g_tops = ops / tg / 1e12
-        rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-                           "us": round(tq * 1e6, 3), "bytes": quantize_bytes(w),
-                           "traffic": measured_traffic("quantize", w.name),
-                           "single_launch_us": kernel_spread(quantize)}
-        rec["roofline"] = {"bound": "mfma", "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS,
-                           "unit": "TFLOP/s", "frac": round(g_tops / INT8_PEAK_TOPS, 4),
-                           "traffic": measured_traffic("gemm", w.name),
-                           "kernel": "gemm_i8 (contraction + fused reconstruction)",
-                           "us": round(tg * 1e6, 3),
-                           "note": "int8 ops: one multiply-add counts as 2",
-                           "single_launch_us": kernel_spread(gemm)}
-    else:
-        rec["roofline"] = None
-        rec["quantize"] = None
+    # per-kernel figures: the quantize pass of the first packed tensor and the
+    # GEMM launch of that tensor (for qkv: the grouped launch of its three
+    # alpha = 1 linears), each launched K times back to back
+    tq = kernel_us(quantize) * 1e-6
+    tg = kernel_us(gemm) * 1e-6
+    n_first = sum(1 for a in w.input_scales if a == scales[0])
+    g_ops = gemm_ops(w, 2 if w.swiglu else n_first)
+    q_gbs = quantize_bytes(w) / tq / 1e9
+    g_tops = g_ops / tg / 1e12
+    rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                       "us": round(tq * 1e6, 3), "bytes": quantize_bytes(w),
+                       "traffic": measured_traffic("quantize", w.name),
+                       "single_launch_us": kernel_spread(quantize)}
+    rec["roofline"] = {"bound": "mfma", "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS,
+                       "unit": "TOPS", "frac": round(g_tops / INT8_PEAK_TOPS, 4),
+                       "traffic": measured_traffic("gemm", w.name),
+                       "kernel": "gemm_i8 (contraction + fused reconstruction)"
+                                 + (f", one grouped launch of {n_first} linears" if n_first > 1 else ""),
+                       "ops": g_ops, "us": round(tg * 1e6, 3),
+                       "note": "int8 ops: one multiply-add counts as 2",
+                       "single_launch_us": kernel_spread(gemm)}
+    if n_packed > 1:
+        t2 = kernel_us(lambda i: gemm(i, 1)) * 1e-6
+        o2 = gemm_ops(w, w.n_linears - n_first)
+        rec["roofline"]["second_gemm"] = {
+            "what": f"the {w.n_linears - n_first} linear(s) at input scale {scales[1]}: "
+                    "own quantize pass (pre-scale) and the division in the epilogue",
+            "us": round(t2 * 1e6, 3), "achieved": round(o2 / t2 / 1e12, 1),
+            "frac": round(o2 / t2 / 1e12 / INT8_PEAK_TOPS, 4)}
+    # the quantize pass against a plain copy of the same bytes: the probe
+    # kernel reads X ([M, K], bf16 or binary32) with 16-byte loads and writes
+    # one byte per element with 16-byte stores, no arithmetic, back to back
+    # over the same input sets
+    if not w.glu and not args.no_probe:
+        probe = probe_library()
+        esz = 2 if w.x_dtype == workloads.BF16 else 4
+        dst = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
+
+        def copy(i):
+            rc = probe.convrot_probe_copy(sets[i % n_sets]["X"].data_ptr(), esz, w.M * w.K,
+                                          dst.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"convrot_probe_copy: hip error {rc}")
+        copy(0)
+        tc = kernel_us(copy) * 1e-6
+        cbytes = w.M * w.K * (esz + 1)
+        rec["quantize"]["copy_ceiling"] = {
+            "what": "probe kernel: the same read of X and write of M x K bytes, 16-byte loads and "
+                    "stores, no arithmetic",
+            "us": round(tc * 1e6, 3), "gbs": round(cbytes / tc / 1e9, 1),
+            "frac": round(cbytes / tc / 1e9 / HBM_PEAK_GBS, 4),
+            "quantize_vs_copy": round(tc / tq, 4)}
+    # the MFMA rate on these codes with no data movement (the power-limited
+    # ceiling of the contraction), in the GEMM's wave shape and occupancy
+    if w.w_bits == 8 and not args.no_probe:
+        rec["roofline"]["mfma_ceiling"] = mfma_ceiling(cr, torch, sets[0]["views"][0][0],
+                                                       sets[0]["lins"][0]["Qw"], g_tops)
+    if shared:
+        warm(step_folded)
+        wall_f, _ = timed(step_folded, args.steps)
+        ms_f = wall_f * 1e3 / args.steps
+        rec["extension"] = {
+            "what": "the same step through convrot_int8_linear_shared, which folds the power-of-two "
+                    "input scale into the alpha = 1 pass (one quantize pass, one grouped GEMM launch "
+                    "of all linears; an extension beyond the pages)",
+            "ms_per_step": round(ms_f, 5), "value": round(ops / (ms_f * 1e-3) / 1e12, 3),
+            "unit": "TOPS"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows or w.M)
     print(json.dumps(rec), flush=True)
@@ -427,6 +542,61 @@ def main() -> int:
             torch.neg(src, out=dst)          # one read and one write of each element
         torch.cuda.synchronize()
     return 0
+
+
+_PROBE = None
+
+
+def probe_library():
+    """libconvrot_probe.so: the measurement kernels (MFMA rate, plain copy)."""
+    global _PROBE
+    if _PROBE is None:
+        from int8_hadamard_rotated_amd import _build
+        lib = ctypes.CDLL(_build.PROBE_LIBRARY)
+        lib.convrot_probe_mfma.restype = ctypes.c_int
+        lib.convrot_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        lib.convrot_probe_copy.restype = ctypes.c_int
+        lib.convrot_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        _PROBE = lib
+    return _PROBE
+
+
+def mfma_ceiling(cr, torch, qx, qw, gemm_tops: float) -> dict:
+    """Run the probe kernel (libconvrot_probe.so) on the workload's own codes:
+    256 workgroups of 8 waves (one per CU), each wave 32 MFMAs per step on
+    register-resident fragments, long enough to reach the power-limited clock."""
+    lib = probe_library()
+    blocks, steps = 256, 2048
+    out = torch.empty(blocks * 512, dtype=torch.int32, device=qx.device)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rc = lib.convrot_probe_mfma(qx.data_ptr(), qx.numel(), qw.data_ptr(), qw.numel(), steps,
+                                    blocks, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"convrot_probe_mfma: hip error {rc}")
+
+    for _ in range(20):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record(stream)
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / n
+    ops = blocks * 8 * steps * 32 * (2 * 16 * 16 * 64)
+    tops = ops / t / 1e12
+    return {"what": "probe: the GEMM's wave shape and occupancy (8 waves, one workgroup per CU), "
+                    "32 MFMAs per step on fragments of this workload's codes held in registers, no "
+                    "loads, LDS traffic or barriers",
+            "achieved": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4),
+            "us": round(t * 1e6, 2), "gemm_of_ceiling": round(gemm_tops / tops, 4)}
 
 
 if __name__ == "__main__":

@@ -156,6 +156,16 @@ typedef struct {
     int64_t ldy;          /* output row stride in elements (>= N) */
 } convrot_linear_desc;
 
+/* Several INT8 linears on one already-quantized input, in one GEMM launch
+ * (the contraction and reconstruction of int8_linear for each; page "INT8
+ * Convrot Safetensors", section "How INT8 convrot works": one packed
+ * activation tensor reused by the linears that share it).  Qx, s_x as for
+ * int8_linear; descs is host memory, 1 <= n <= 16, and each linear's
+ * input_scale is its divisor (as int8_linear's).  Outputs must not overlap
+ * each other, Qx, s_x or any weight-side input. */
+int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, int n,
+                        const convrot_linear_desc *descs, void *stream);
+
 /* Several linears on the same X and group size.  Every distinct input scale
  * gets one quantization pass (all alpha = 1 linears share one packed tensor,
  * as the page prescribes; linears with equal alpha != 1 also share, which

@@ -155,6 +155,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                                       i64, vp, sz, vp]),
         "convrot_int8_linear_noalloc": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp, i64, vp,
                                               i32, i64, vp]),
+        "int8_linear_grouped": (i32, [vp, vp, i64, i64, i32, ctypes.POINTER(LinearDesc), vp]),
         "convrot_int8_linear_shared": (i32, [vp, i32, i64, i64, i64, i32, i32,
                                              ctypes.POINTER(LinearDesc), vp, sz, vp]),
         "convrot_int8_linear_shared_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc),
@@ -403,6 +404,42 @@ def convrot_int8_linear(X, group_size: int, input_scale: float, Qw, s_w=None, bi
                                        workspace.numel(), _stream(stream, X))
     _check("convrot_int8_linear", rc)
     return Y
+
+
+def _descs(M: int, linears, device):
+    torch = _torch()
+    n = len(linears)
+    descs = (LinearDesc * max(n, 1))()
+    outs = []
+    for i, lin in enumerate(linears):
+        Qw = lin["Qw"]
+        N = Qw.shape[0]
+        Y = lin.get("Y")
+        if Y is None:
+            Y = torch.empty((M, N), dtype=_torch_dtype(lin.get("y_dtype", F32)), device=device)
+        outs.append(Y)
+        descs[i].Qw = Qw.data_ptr()
+        descs[i].s_w = lin["s_w"].data_ptr() if lin.get("s_w") is not None else None
+        descs[i].bias = lin["bias"].data_ptr() if lin.get("bias") is not None else None
+        descs[i].N = N
+        descs[i].input_scale = float(lin.get("input_scale", 1.0))
+        descs[i].Y = Y.data_ptr()
+        descs[i].y_dtype = _dtype_code(Y)
+        descs[i].ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+    return descs, outs
+
+
+def int8_linear_grouped(Qx, s_x, linears, M: int | None = None, stream=None):
+    """Several linears on one quantized input in one GEMM launch.  ``linears``:
+    dicts with Qw, s_w, bias, input_scale (the divisor) and optionally Y /
+    y_dtype.  Returns the outputs."""
+    M = Qx.shape[0] if M is None else M
+    K = Qx.shape[1]
+    descs, outs = _descs(M, linears, Qx.device)
+    rc = library().int8_linear_grouped(_ptr(Qx), _ptr(s_x), M, K, len(linears), descs,
+                                       _stream(stream, Qx))
+    _check("int8_linear_grouped", rc)
+    return outs
 
 
 def convrot_int8_linear_noalloc(X, group_size: int, input_scale: float, Qw, s_w=None, bias=None,

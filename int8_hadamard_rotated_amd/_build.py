@@ -12,6 +12,10 @@ CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libconvrot.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["convrot_api.cpp", "quantize.hip", "gemm_i8.hip", "static_workspace.hip"]
+# the measurement probes of the roofline report (MFMA rate, plain copy), a
+# library of their own
+PROBE_SOURCE = "probes.hip"
+PROBE_LIBRARY = os.path.join(PKG, "libconvrot_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -62,8 +66,13 @@ def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool =
     shared library; refuse a build in which any kernel spills registers."""
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=len(srcs)) as pool:
-        results = list(pool.map(lambda s: _compile(s, list(extra or [])), srcs))
+    probe_src = os.path.join(CSRC, PROBE_SOURCE)
+    with ThreadPoolExecutor(max_workers=len(srcs) + 1) as pool:
+        results = list(pool.map(lambda s: _compile(s, list(extra or [])), srcs + [probe_src]))
+    probe_obj, probe_res = results.pop()
+    if probe_res.returncode != 0:
+        sys.stderr.write(probe_res.stdout + probe_res.stderr)
+        raise RuntimeError(f"hipcc failed ({probe_res.returncode}) on {probe_src}")
     remarks = ""
     for src, (obj, res) in zip(srcs, results):
         if res.returncode != 0:
@@ -84,6 +93,13 @@ def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool =
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"link failed ({res.returncode}): {' '.join(cmd)}")
     os.replace(tmp, output)
+    if output == LIBRARY:
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", PROBE_LIBRARY + ".tmp"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"link failed ({res.returncode}): {' '.join(cmd)}")
+        os.replace(PROBE_LIBRARY + ".tmp", PROBE_LIBRARY)
     return output
 
 

@@ -3,6 +3,7 @@
 // include/convrot.h.  Nothing here allocates device memory or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -18,6 +19,26 @@ constexpr int64_t kMaxContractionK = 133120;   // largest multiple of 64 with K 
 constexpr int64_t kMaxContractionK4 = 132096;  // largest multiple of 64 with 16 * K * 127 * 8 < 2^31
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Every row count, column count and row stride is at most 2^30, so that all
+// byte extents below fit in int64 (2^30 rows x 2^30 strides x 4 bytes).
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool dim_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
+
+// The GEMM numbers its 128 x 128 tiles (the smallest it uses) with an int.
+int64_t tiles_of(int64_t M, int64_t cols) { return ((M + 127) / 128) * ((cols + 127) / 128); }
+
+bool tiles_ok(int64_t M, int64_t cols) { return tiles_of(M, cols) <= INT32_MAX; }
+
+// Linears of one grouped launch share the tile numbering.
+bool group_tiles_ok(int64_t M, int n, const convrot_linear_desc *descs)
+{
+    int64_t t = 0;
+    for (int i = 0; i < n; ++i)
+        t += tiles_of(M, 2 * descs[i].N);
+    return t <= INT32_MAX;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -71,7 +92,7 @@ int check_quantizer_shape(int64_t K, int G)
 int check_quantize_args(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
                         float alpha)
 {
-    if (M < 0 || K < 1 || ldx < K)
+    if (M < 0 || K < 1 || ldx < K || !dim_ok(M) || !dim_ok(ldx))
         return CONVROT_EINVAL;
     if (!dtype_ok(x_dtype))
         return CONVROT_EUNSUPPORTED;
@@ -94,7 +115,7 @@ int check_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t 
                  int64_t N, float alpha, const void *Y, int y_dtype, int64_t ldy, bool need_scales,
                  LinearCheck *out, int w_bits = 8)
 {
-    if (N < 0 || ldy < N)
+    if (N < 0 || ldy < N || !dim_ok(M) || !dim_ok(ldy) || !tiles_ok(M, 2 * N))
         return CONVROT_EINVAL;
     if (need_scales && !dtype_ok(y_dtype))
         return CONVROT_EUNSUPPORTED;
@@ -169,7 +190,8 @@ int check_gated_act(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, P
     if (pre->act != CONVROT_ACT_SILU && pre->act != CONVROT_ACT_SIGMOID)
         return CONVROT_EUNSUPPORTED;
     const int64_t esz = elem_bytes(x_dtype);
-    if (!pre->up || !aligned(pre->up, 16) || pre->ld_up < K || (pre->ld_up * esz) % 16 != 0)
+    if (!pre->up || !aligned(pre->up, 16) || pre->ld_up < K || !dim_ok(pre->ld_up) ||
+        (pre->ld_up * esz) % 16 != 0)
         return CONVROT_EINVAL;
     if (K > quantize_max_k(K, true))
         return CONVROT_EUNSUPPORTED;
@@ -218,7 +240,7 @@ extern "C" {
 
 size_t convrot_packed_bytes(int64_t M, int64_t K)
 {
-    if (M < 0 || K < 1)
+    if (M < 0 || K < 1 || !dim_ok(M) || !dim_ok(K))
         return 0;
     const int64_t m_pad = round_up(M, 4);
     return (size_t)(m_pad * K + 4 * m_pad);
@@ -228,7 +250,11 @@ size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed)
 {
     if (n_packed < 0)
         return 0;
-    return (size_t)n_packed * (size_t)round_up((int64_t)convrot_packed_bytes(M, K), 256);
+    size_t bytes = 0;
+    if (__builtin_mul_overflow((size_t)n_packed, (size_t)round_up((int64_t)convrot_packed_bytes(M, K), 256),
+                               &bytes))
+        return 0;
+    return bytes;
 }
 
 int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -294,7 +320,7 @@ int check_post(const convrot_post *post, int64_t M, int64_t N, const void *Y, in
         return CONVROT_OK;
     const int64_t e = elem_bytes(y_dtype);
     if (!post->gate || !aligned(post->gate, 4) || !post->residual ||
-        !aligned(post->residual, (uintptr_t)e) || post->ld_residual < N)
+        !aligned(post->residual, (uintptr_t)e) || post->ld_residual < N || !dim_ok(post->ld_residual))
         return CONVROT_EINVAL;
     const Span rs = rows_span(post->residual, M, N, post->ld_residual, e);
     const bool in_place = post->residual == Y && post->ld_residual == ldy;
@@ -413,6 +439,59 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
     return linear_impl(Qx, s_x, M, K, Qw, s_w, bias, N, input_scale, Y, y_dtype, ldy, stream, 8);
 }
 
+int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, int n,
+                        const convrot_linear_desc *descs, void *stream)
+{
+    if (M < 0 || n < 1 || n > kMaxLinears || !descs)
+        return CONVROT_EINVAL;
+    int rc = check_contraction_k(K, 8);
+    if (rc != CONVROT_OK)
+        return rc;
+    LinearCheck chk[kMaxLinears];
+    for (int i = 0; i < n; ++i) {
+        const convrot_linear_desc &d = descs[i];
+        rc = check_linear(d.Qw, d.s_w, d.bias, M, K, d.N, d.input_scale, d.Y, d.y_dtype, d.ldy,
+                          true, &chk[i]);
+        if (rc != CONVROT_OK)
+            return rc;
+    }
+    if (!group_tiles_ok(M, n, descs))
+        return CONVROT_EINVAL;
+    if (M == 0)
+        return CONVROT_OK;
+    if (!Qx || !s_x || !aligned(Qx, 16) || !aligned(s_x, 4))
+        return CONVROT_EINVAL;
+    const Span qx = span_of(Qx, M * K), sx = span_of(s_x, 4 * M);
+    for (int i = 0; i < n; ++i) {
+        if (overlap(chk[i].y, qx) || overlap(chk[i].y, sx))
+            return CONVROT_EOVERLAP;
+        for (int k = 0; k < n; ++k) {
+            if (y_hits_weights(chk[i], chk[k]))
+                return CONVROT_EOVERLAP;
+            if (k != i && overlap(chk[i].y, chk[k].y))
+                return CONVROT_EOVERLAP;
+        }
+    }
+    GemmProblem p;
+    std::memset(&p, 0, sizeof p);
+    p.Qx = Qx;
+    p.s_x = s_x;
+    p.M = M;
+    p.K = K;
+    p.w_bits = 8;
+    for (int i = 0; i < n; ++i) {
+        const convrot_linear_desc &d = descs[i];
+        if (d.N == 0)
+            continue;
+        p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, d.input_scale, d.Y,
+                                       out_kind_of(d.y_dtype), d.ldy);
+    }
+    if (p.n_lin == 0)
+        return CONVROT_OK;
+    (void)hipGetLastError();
+    return hip_status(launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
 int int8_swiglu_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K,
                        const int8_t *Qw_gate, const float *s_w_gate, const int8_t *Qw_up,
                        const float *s_w_up, int64_t N, float input_scale, void *Y, int y_dtype,
@@ -525,6 +604,8 @@ int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
             scales[n_slots++] = a;
         slot_of[i] = s;
     }
+    if (!group_tiles_ok(M, n, descs))
+        return CONVROT_EINVAL;
     if (M == 0)
         return CONVROT_OK;
 

@@ -21,8 +21,16 @@ __device__ __forceinline__ void wave_lds_sync()
 // ---------------------------------------------------------------- quantize
 // Largest row (in elements) the quantizer handles for a given K: one
 // workgroup per group of rows, at most 256 quads of 4 lanes per row (128 with
-// the RMSNorm producer).
-int64_t quantize_max_k(int64_t K, bool rmsnorm = false);
+// the RMSNorm producer); a quad covers 256, 128 or 64 elements.
+inline int64_t quantize_max_k(int64_t K, bool rmsnorm = false)
+{
+    const int64_t quads = rmsnorm ? 128 : 256;
+    if (K % 256 == 0)
+        return quads * 256;
+    if (K % 128 == 0)
+        return quads * 128;
+    return quads * 64;
+}
 
 // Producer applied to each widened input element before the rotation.
 enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2, kPreGatedAct = 3 };

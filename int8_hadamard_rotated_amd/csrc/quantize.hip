@@ -989,18 +989,6 @@ __global__ __launch_bounds__(256) void expf_kernel(const float *x, float *y, int
 
 }  // namespace
 
-int64_t quantize_max_k(int64_t K, bool rmsnorm)
-{
-    // 256 quads per row at most (128 with RMSNorm); a quad covers 256, 128
-    // or 64 elements.
-    const int64_t quads = rmsnorm ? 128 : 256;
-    if (K % 256 == 0)
-        return quads * 256;
-    if (K % 128 == 0)
-        return quads * 128;
-    return quads * 64;
-}
-
 hipError_t launch_expf(const float *x, float *y, int64_t n, hipStream_t stream)
 {
     const int64_t blocks = (n + 255) / 256;

@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
         "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf",
-        "int8_swiglu_linear", "convrot_int8_linear_noalloc"])
+        "int8_swiglu_linear", "convrot_int8_linear_noalloc", "int8_linear_grouped"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -314,6 +314,36 @@ def test_fused_validation(lib):
     assert f(*args(BASE + 128 * MB, BASE + 256 * MB, need - 16)) == EWS
     assert f(*args(BASE + 64 * MB, BASE + 256 * MB, need)) == EOVL          # Y on the weights
     assert f(*args(BASE + 256 * MB, BASE + 256 * MB, need)) == EOVL         # Y on the workspace
+
+
+def test_grouped_validation(lib):
+    """int8_linear_grouped: count, shapes and overlaps, before any HIP call."""
+    f = lib.int8_linear_grouped
+    Qx, sx = BASE, BASE + 16 * MB
+    W1, W2, Y1, Y2 = BASE + 64 * MB, BASE + 96 * MB, BASE + 128 * MB, BASE + 192 * MB
+
+    def desc(W, Y, N=32, a=1.0, ld=None):
+        d = cr.LinearDesc()
+        d.Qw, d.s_w, d.bias, d.N, d.input_scale = W, None, None, N, a
+        d.Y, d.y_dtype, d.ldy = Y, cr.F32, N if ld is None else ld
+        return d
+
+    def call(ds, M=8, K=256, n=None, qx=Qx):
+        arr = (cr.LinearDesc * max(len(ds), 1))(*ds)
+        return f(ctypes.c_void_p(qx), ctypes.c_void_p(sx), M, K, len(ds) if n is None else n, arr, None)
+
+    good = [desc(W1, Y1), desc(W2, Y2)]
+    assert call(good, n=0) == EINVAL
+    assert call(good, n=17) == EINVAL
+    assert call(good, K=250) == EUNSUP
+    assert call(good, K=133120 + 64) == EOVF
+    assert call([desc(W1, Y1), desc(W2, Y1 + 64)]) == EOVL            # outputs overlap
+    assert call([desc(W1, Y1), desc(W2, W1 + 128)]) == EOVL           # output on a weight
+    assert call(good, qx=Y1) == EOVL                                   # output on Q_x
+    assert call([desc(W1, Y1, a=0.0)]) == EINVAL
+    assert call([desc(W1, Y1, ld=16)]) == EINVAL                       # ldy < N
+    assert call(good, qx=0) == EINVAL
+    assert call(good, M=0) == OK
 
 
 def test_noalloc_validation(lib):

@@ -129,6 +129,35 @@ def test_int8_linear_big_grid_unscale(orc, y_dtype):
     check_y(host(Yf), want, y_dtype, f"fused Y {M}x{K}x{N} alpha={alpha}")
 
 
+@pytest.mark.parametrize("M,K,Ns", [(515, 768, (130, 64, 257)), (1030, 512, (3072, 3072, 3072))])
+def test_int8_linear_grouped(orc, M, K, Ns):
+    """Several linears on one packed input in one launch, each with its own
+    divisor, output dtype and row stride; the second shape is 180 tiles of
+    256 x 256 (the 256 x 256 kernel with the division compiled in)."""
+    import torch
+    rng = np.random.default_rng(M + K)
+    G = 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    p = orc.quantize_rows(X, G, threads=THREADS)
+    alphas = (1.0, 0.3, 1.0)
+    dtypes = (oracle.BF16, oracle.F32, oracle.F32)
+    lins, wants = [], []
+    for N, a, yd in zip(Ns, alphas, dtypes):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        A = orc.gemm_i32(p.q, Qw, threads=THREADS)
+        wants.append(orc.epilogue(A, p.s, sw, b, a, yd, threads=THREADS))
+        lins.append(dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=yd))
+    # the last output strided inside a wider buffer
+    wide = torch.full((M, Ns[2] + 5), -7.0, dtype=torch.float32, device="cuda:0")
+    lins[2]["Y"] = wide[:, :Ns[2]]
+    say("int8_linear_grouped", M, K, Ns)
+    outs = cr.int8_linear_grouped(dev(p.q), dev(p.s), lins)
+    for j, (y, want, yd) in enumerate(zip(outs, wants, dtypes)):
+        check_y(np.ascontiguousarray(host(y)), want, yd, f"grouped linear {j}")
+    assert np.all(host(wide)[:, Ns[2]:] == -7.0), "wrote past N"
+
+
 def test_int8_linear_strided_output(orc):
     """ldy > N, and an output whose rows do not allow vector stores."""
     rng = np.random.default_rng(5)
