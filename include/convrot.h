@@ -84,12 +84,19 @@ typedef enum {
 
 typedef enum { CONVROT_F32 = 0, CONVROT_BF16 = 1 } convrot_dtype;
 
-/* Bytes of the packed activation tensor for M rows of K features:
+/* Bytes of the packed activation tensor for M rows of K features (page
+ * "ggml operator extensions", section "sd.cpp integration": I8 rows padded
+ * to a multiple of four, followed by the F32 row scales):
  * int8 codes [M_pad][K] followed by float scales [M_pad], M_pad = 4*ceil(M/4).
- * Pad rows hold zero codes and a zero scale.  Returns 0 if M < 0 or K < 1. */
+ * Pad rows hold zero codes and a zero scale.  Returns 0 if M < 0, K < 1, or
+ * M or K is above 2^30 (every dimension and row stride of this interface is
+ * at most 2^30; larger ones are CONVROT_EINVAL). */
 size_t convrot_packed_bytes(int64_t M, int64_t K);
 
-/* Rotate, quantize and pack M rows of X.
+/* Rotate, quantize and pack M rows of X (page "INT8 Convrot Safetensors",
+ * section "How INT8 convrot works": the group-wise rotation and, in
+ * "Runtime activation quantization", the per-row scale and codes; packed as
+ * convrot_packed_bytes describes).
  *   X           [M][ldx] f32 or bf16 (x_dtype), first K columns used
  *   group_size  G, rotation group (power of four dividing K)
  *   input_scale alpha > 0, finite; X is multiplied by it before the rotation
@@ -99,7 +106,11 @@ size_t convrot_packed_bytes(int64_t M, int64_t K);
 int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                           int group_size, float input_scale, void *packed, void *stream);
 
-/* INT8 linear on already-quantized activations (the GEMM + reconstruction):
+/* INT8 linear on already-quantized activations, the GEMM + reconstruction
+ * (page "INT8 Convrot Safetensors", section "How INT8 convrot works": the
+ * int32 accumulation and Y = A s_x s_w + b; page "ggml operator extensions",
+ * section "sd.cpp integration": the order float(A) * s_x * s_w + bias with
+ * nullable weight scale and bias):
  *   Y = fl(fl(fl(fl(float(Q_x Q_w^T)) * s_x) * s_w) / input_scale) + bias
  *   Qx     [M][K] int8 codes (row stride K); for a packed tensor pass its base
  *   s_x    [M] float row scales; for a packed tensor pass base + M_pad * K
@@ -114,10 +125,14 @@ int int8_linear(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, const 
                 int y_dtype, int64_t ldy, void *stream);
 
 /* Workspace bytes needed by the fused entries for `n_packed` packed tensors of
- * M rows x K features (each rounded up to 256 bytes). */
+ * M rows x K features (each rounded up to 256 bytes); 0 when that does not fit
+ * a size_t.  The workspace is the framework's, never the library's (page
+ * "ggml operator extensions", section "Backend services"). */
 size_t convrot_workspace_bytes(int64_t M, int64_t K, int n_packed);
 
-/* The fused layer for one linear: convrot_quantize_rows into the workspace,
+/* The fused layer for one linear (page "INT8 Convrot Safetensors", section
+ * "How INT8 convrot works", the whole layer including the input scale):
+ * convrot_quantize_rows into the workspace,
  * then int8_linear on it (a power-of-two input scale is folded as in
  * convrot_int8_linear_shared).  workspace >= convrot_workspace_bytes(M, K, 1);
  * contents are not preserved between calls.  Y may alias X (X is fully
@@ -166,7 +181,11 @@ typedef struct {
 int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, int n,
                         const convrot_linear_desc *descs, void *stream);
 
-/* Several linears on the same X and group size.  Every distinct input scale
+/* Several linears on the same X and group size (page "INT8 Convrot
+ * Safetensors", section "How INT8 convrot works", last paragraph: one
+ * quantized activation reused by the linears that share it; page "ggml
+ * operator extensions", section "sd.cpp integration": F32 or packed input).
+ * Every distinct input scale
  * gets one quantization pass (all alpha = 1 linears share one packed tensor,
  * as the page prescribes; linears with equal alpha != 1 also share, which
  * gives the same bits as separate passes); then one grouped GEMM launch per
@@ -265,7 +284,9 @@ int convrot_int8_linear_shared_pre(const void *X, int x_dtype, int64_t M, int64_
                                    const convrot_linear_desc *descs, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
-/* The raw int32 accumulator A = Q_x Q_w^T (same contraction kernel as
+/* The raw int32 accumulator A = Q_x Q_w^T of page "INT8 Convrot
+ * Safetensors", section "Runtime activation quantization" (same contraction
+ * kernel as
  * int8_linear, with the reconstruction replaced by an int32 store); for
  * checking the contraction bit for bit.  A is [M][N] int32. */
 int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t K, int64_t N,
@@ -345,7 +366,9 @@ int convrot_int4_gemm_i32(const int8_t *Qx, const uint8_t *W4, int64_t M, int64_
  * checked against a reference directly. */
 int convrot_expf(const float *x, float *y, int64_t n, void *stream);
 
-/* Static, human-readable text for a status code. */
+/* Static, human-readable text for a status code (errors are reported, never
+ * retried or hidden behind a fallback: page "ggml operator extensions",
+ * section "Kernel selection"). */
 const char *convrot_status_string(int status);
 
 #ifdef __cplusplus

@@ -376,8 +376,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            if (dma && i < T::kLoads)
-                issue_one(dma_step, i);
+            // The wave's DMA loads are spread evenly over the step's MFMA
+            // groups.  Issued back to back in the first groups, every wave's
+            // loads reach the vector memory queue at once; spread, mlp_up
+            // ran 0.3-1.3% faster for the same bytes.
+            constexpr int kEvery = T::kTM / T::kLoads;
+            if (dma && i % kEvery == 0 && i / kEvery < T::kLoads)
+                issue_one(dma_step, i / kEvery);
             if constexpr (WB == 4) {
                 if (i == (T::kTM > 1 ? 1 : 0) && expand)
                     write_expanded(k + 2, pk);
