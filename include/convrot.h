@@ -169,15 +169,22 @@ typedef struct {
     void *Y;              /* [M][ldy] output (device) */
     int y_dtype;          /* CONVROT_F32 or CONVROT_BF16 */
     int64_t ldy;          /* output row stride in elements (>= N) */
+    const int8_t *Qx;     /* int8_linear_grouped only: this linear's own quantized
+                             input [M][K] (device), or NULL for the call's Qx;
+                             NULL for the fused entries, which quantize X */
+    const float *s_x;     /* with Qx: its [M] row scales (device); else NULL */
 } convrot_linear_desc;
 
-/* Several INT8 linears on one already-quantized input, in one GEMM launch
- * (the contraction and reconstruction of int8_linear for each; page "INT8
+/* Several INT8 linears on already-quantized inputs, in one GEMM launch (the
+ * contraction and reconstruction of int8_linear for each; page "INT8
  * Convrot Safetensors", section "How INT8 convrot works": one packed
  * activation tensor reused by the linears that share it).  Qx, s_x as for
- * int8_linear; descs is host memory, 1 <= n <= 16, and each linear's
- * input_scale is its divisor (as int8_linear's).  Outputs must not overlap
- * each other, Qx, s_x or any weight-side input. */
+ * int8_linear: the input of every linear whose descriptor leaves Qx NULL; a
+ * linear may name its own (Qx, s_x) instead, e.g. the packed tensor of its
+ * own input scale, of the same M and K.  descs is host memory, 1 <= n <= 16,
+ * and each linear's input_scale is its divisor (as int8_linear's).  Outputs
+ * must not overlap each other, any input codes or scales, or any weight-side
+ * input. */
 int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K, int n,
                         const convrot_linear_desc *descs, void *stream);
 
@@ -188,8 +195,9 @@ int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K
  * Every distinct input scale
  * gets one quantization pass (all alpha = 1 linears share one packed tensor,
  * as the page prescribes; linears with equal alpha != 1 also share, which
- * gives the same bits as separate passes); then one grouped GEMM launch per
- * packed tensor covers all linears that read it.
+ * gives the same bits as separate passes); then one grouped GEMM launch
+ * covers every linear, each reading the packed tensor of its scale.  The
+ * descriptors' Qx and s_x must be NULL.
  *
  * A power-of-two input scale 2^k with |k| <= 16 counts as alpha = 1: such a
  * linear reads the alpha = 1 packed tensor and its reconstruction skips the

@@ -41,6 +41,8 @@ class LinearDesc(ctypes.Structure):
         ("Y", ctypes.c_void_p),
         ("y_dtype", ctypes.c_int),
         ("ldy", ctypes.c_int64),
+        ("Qx", ctypes.c_void_p),
+        ("s_x", ctypes.c_void_p),
     ]
 
 
@@ -426,13 +428,17 @@ def _descs(M: int, linears, device):
         descs[i].Y = Y.data_ptr()
         descs[i].y_dtype = _dtype_code(Y)
         descs[i].ldy = _row_stride(Y) if M > 0 and N > 0 else max(N, 1)
+        if lin.get("Qx") is not None:
+            descs[i].Qx = lin["Qx"].data_ptr()
+            descs[i].s_x = lin["s_x"].data_ptr()
     return descs, outs
 
 
 def int8_linear_grouped(Qx, s_x, linears, M: int | None = None, stream=None):
-    """Several linears on one quantized input in one GEMM launch.  ``linears``:
+    """Several linears on quantized inputs in one GEMM launch.  ``linears``:
     dicts with Qw, s_w, bias, input_scale (the divisor) and optionally Y /
-    y_dtype.  Returns the outputs."""
+    y_dtype, and Qx / s_x for a linear that reads its own quantized input
+    instead of the call's.  Returns the outputs."""
     M = Qx.shape[0] if M is None else M
     K = Qx.shape[1]
     descs, outs = _descs(M, linears, Qx.device)

@@ -457,15 +457,36 @@ int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K
     }
     if (!group_tiles_ok(M, n, descs))
         return CONVROT_EINVAL;
+    // each linear's input: its own (Qx, s_x) or the call's
+    const int8_t *qx_of[kMaxLinears];
+    const float *sx_of[kMaxLinears];
+    bool shared_used = false;
+    for (int i = 0; i < n; ++i) {
+        if ((descs[i].Qx == nullptr) != (descs[i].s_x == nullptr))
+            return CONVROT_EINVAL;
+        qx_of[i] = descs[i].Qx ? descs[i].Qx : Qx;
+        sx_of[i] = descs[i].Qx ? descs[i].s_x : s_x;
+        shared_used = shared_used || (descs[i].Qx == nullptr && descs[i].N > 0);
+    }
     if (M == 0)
         return CONVROT_OK;
-    if (!Qx || !s_x || !aligned(Qx, 16) || !aligned(s_x, 4))
+    if (shared_used && (!Qx || !s_x))
         return CONVROT_EINVAL;
-    const Span qx = span_of(Qx, M * K), sx = span_of(s_x, 4 * M);
     for (int i = 0; i < n; ++i) {
-        if (overlap(chk[i].y, qx) || overlap(chk[i].y, sx))
-            return CONVROT_EOVERLAP;
+        if (descs[i].N == 0)
+            continue;
+        if (!aligned(qx_of[i], 16) || !aligned(sx_of[i], 4))
+            return CONVROT_EINVAL;
+    }
+    for (int i = 0; i < n; ++i) {
+        if (descs[i].N == 0)
+            continue;
         for (int k = 0; k < n; ++k) {
+            if (descs[k].N == 0)
+                continue;
+            if (overlap(chk[i].y, span_of(qx_of[k], M * K)) ||
+                overlap(chk[i].y, span_of(sx_of[k], 4 * M)))
+                return CONVROT_EOVERLAP;
             if (y_hits_weights(chk[i], chk[k]))
                 return CONVROT_EOVERLAP;
             if (k != i && overlap(chk[i].y, chk[k].y))
@@ -474,8 +495,6 @@ int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K
     }
     GemmProblem p;
     std::memset(&p, 0, sizeof p);
-    p.Qx = Qx;
-    p.s_x = s_x;
     p.M = M;
     p.K = K;
     p.w_bits = 8;
@@ -483,8 +502,11 @@ int int8_linear_grouped(const int8_t *Qx, const float *s_x, int64_t M, int64_t K
         const convrot_linear_desc &d = descs[i];
         if (d.N == 0)
             continue;
-        p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, d.input_scale, d.Y,
-                                       out_kind_of(d.y_dtype), d.ldy);
+        GemmLinear l = make_linear(d.Qw, d.s_w, d.bias, d.N, d.input_scale, d.Y,
+                                   out_kind_of(d.y_dtype), d.ldy);
+        l.Qx = qx_of[i];
+        l.s_x = sx_of[i];
+        p.lin[p.n_lin++] = l;
     }
     if (p.n_lin == 0)
         return CONVROT_OK;
@@ -565,7 +587,7 @@ int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t
 namespace {
 
 // The fused entries: validation, one quantization pass per distinct input
-// scale into the workspace, then one grouped GEMM launch per packed tensor.
+// scale into the workspace, then one grouped GEMM launch over all linears.
 // With use_static the workspace is the library's static buffer instead of
 // the caller's (taken only after every other argument has been validated).
 int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -592,6 +614,8 @@ int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
     int n_slots = 0;
     for (int i = 0; i < n; ++i) {
         const convrot_linear_desc &d = descs[i];
+        if (d.Qx || d.s_x)
+            return CONVROT_EINVAL;      // the fused entries quantize X themselves
         rc = check_linear(d.Qw, d.s_w, d.bias, M, K, d.N, d.input_scale, d.Y, d.y_dtype, d.ldy,
                           true, &chk[i]);
         if (rc != CONVROT_OK)
@@ -651,30 +675,28 @@ int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
         if (rc != CONVROT_OK)
             return rc;
     }
+    // one grouped launch: every linear reads the packed tensor of its scale
     const int64_t m_pad = round_up(M, 4);
-    for (int s = 0; s < n_slots; ++s) {
-        GemmProblem p;
-        std::memset(&p, 0, sizeof p);
-        p.Qx = base + s * slot_bytes;
-        p.s_x = reinterpret_cast<const float *>(base + s * slot_bytes + m_pad * K);
-        p.M = M;
-        p.K = K;
-        p.w_bits = 8;
-        for (int i = 0; i < n; ++i) {
-            if (slot_of[i] != s || descs[i].N == 0)
-                continue;
-            const convrot_linear_desc &d = descs[i];
-            // the divisor is the scale of the pass this linear reads
-            p.lin[p.n_lin++] = make_linear(d.Qw, d.s_w, d.bias, d.N, scales[s], d.Y,
-                                           out_kind_of(d.y_dtype), d.ldy);
-        }
-        if (p.n_lin == 0)
+    GemmProblem p;
+    std::memset(&p, 0, sizeof p);
+    p.M = M;
+    p.K = K;
+    p.w_bits = 8;
+    for (int i = 0; i < n; ++i) {
+        const convrot_linear_desc &d = descs[i];
+        if (d.N == 0)
             continue;
-        rc = hip_status(launch_gemm(p, st));
-        if (rc != CONVROT_OK)
-            return rc;
+        const int s = slot_of[i];
+        // the divisor is the scale of the pass this linear reads
+        GemmLinear l = make_linear(d.Qw, d.s_w, d.bias, d.N, scales[s], d.Y,
+                                   out_kind_of(d.y_dtype), d.ldy);
+        l.Qx = base + s * slot_bytes;
+        l.s_x = reinterpret_cast<const float *>(base + s * slot_bytes + m_pad * K);
+        p.lin[p.n_lin++] = l;
     }
-    return CONVROT_OK;
+    if (p.n_lin == 0)
+        return CONVROT_OK;
+    return hip_status(launch_gemm(p, st));
 }
 
 convrot_linear_desc one_linear(const int8_t *Qw, const float *s_w, const float *bias, int64_t N,
@@ -689,6 +711,8 @@ convrot_linear_desc one_linear(const int8_t *Qw, const float *s_w, const float *
     d.Y = Y;
     d.y_dtype = y_dtype;
     d.ldy = ldy;
+    d.Qx = nullptr;
+    d.s_x = nullptr;
     return d;
 }
 

@@ -19,7 +19,8 @@
 // lane-to-K mapping inside an MFMA only has to agree between the two
 // operands, which are read with the same pattern.
 //
-// Several linears sharing one Q_x run in one launch: the tile index space is
+// Several linears run in one launch, each reading the shared Q_x or a packed
+// tensor of its own (one per input scale): the tile index space is
 // the concatenation of every linear's tile grid.  Workgroups are renumbered
 // so that each XCD (round-robin dispatch over 8) receives a contiguous range
 // of tiles, walked in groups of 4 tile rows, so that tiles running together
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int64_t a_rows = (M - m0) < BM ? (M - m0) : BM;
     const int64_t b_span = GLU ? BN / 2 : BN;
     const int64_t b_rows = (N - n0o) < b_span ? (N - n0o) : b_span;
-    const v4u a_rsrc = buffer_rsrc(p.Qx + m0 * K, (uint32_t)(a_rows * K));
+    const v4u a_rsrc = buffer_rsrc(L.Qx + m0 * K, (uint32_t)(a_rows * K));
     const v4u b_rsrc = buffer_rsrc(L.Qw + n0o * kb, (uint32_t)(b_rows * kb));
     const v4u u_rsrc = buffer_rsrc(GLU ? L.Qw_up + n0o * kb : nullptr, GLU ? (uint32_t)(b_rows * kb) : 0u);
     const int ld_row = lane >> 2;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const bool has_post = POST && L.post != 0;
     {
         constexpr int kSeg = (BM + 3 * BN) / 64;
-        const v4u sx_rsrc = buffer_rsrc(want_sx ? p.s_x + m0 : nullptr,
+        const v4u sx_rsrc = buffer_rsrc(want_sx ? L.s_x + m0 : nullptr,
                                         want_sx ? (uint32_t)(a_rows * 4) : 0u);
         const v4u sw_rsrc = buffer_rsrc(has_sw ? L.s_w + n0 : nullptr,
                                         has_sw ? (uint32_t)(b_rows * 4) : 0u);
@@ -598,9 +599,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // The plain and gated-residual epilogue, with the output kind and, for
     // tiles wholly inside Y with vector stores allowed, the absence of bounds
     // checks fixed at compile time (no per-slot branches on either).
-    auto epilogue = [&](auto kind_tag, auto full_tag) {
+    auto epilogue = [&](auto kind_tag, auto full_tag, auto div_tag) {
         constexpr int KIND = decltype(kind_tag)::value;
         constexpr bool FULL = decltype(full_tag)::value;
+        constexpr bool TDIV = decltype(div_tag)::value;
 #pragma unroll
         for (int i = 0; i < T::kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                         float x = (float)a[e];
                         x = x * sxr;
                         x = x * sw[e];
-                        if constexpr (DIV)
+                        if constexpr (TDIV)
                             x = __fdiv_rn(x, alpha);
                         x = x + bo[e];
                         t[e] = x;
@@ -708,19 +710,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             }
         }
     };
+    // A launch compiled with the division may also hold linears whose
+    // divisor is 1 (a grouped launch over several input scales): their tiles
+    // skip it, which gives the same bits (x / 1 is exact) without its cost.
+    auto run = [&](auto kind_tag, auto full_tag) {
+        if constexpr (DIV) {
+            if (alpha != 1.0f) {
+                epilogue(kind_tag, full_tag, std::true_type{});
+                return;
+            }
+        }
+        epilogue(kind_tag, full_tag, std::false_type{});
+    };
     const bool tile_full = L.vec_store != 0 && n0 + BN <= N && m0 + BM <= M;
     if (kind == kOutBF16) {
         if (tile_full)
-            epilogue(std::integral_constant<int, kOutBF16>{}, std::true_type{});
+            run(std::integral_constant<int, kOutBF16>{}, std::true_type{});
         else
-            epilogue(std::integral_constant<int, kOutBF16>{}, std::false_type{});
+            run(std::integral_constant<int, kOutBF16>{}, std::false_type{});
     } else if (kind == kOutF32) {
         if (tile_full)
-            epilogue(std::integral_constant<int, kOutF32>{}, std::true_type{});
+            run(std::integral_constant<int, kOutF32>{}, std::true_type{});
         else
-            epilogue(std::integral_constant<int, kOutF32>{}, std::false_type{});
+            run(std::integral_constant<int, kOutF32>{}, std::false_type{});
     } else {
-        epilogue(std::integral_constant<int, kOutI32>{}, std::false_type{});
+        epilogue(std::integral_constant<int, kOutI32>{}, std::false_type{}, std::false_type{});
     }
 }
 
@@ -733,6 +747,10 @@ hipError_t launch_tiled(GemmProblem p, hipStream_t stream)
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     int total = 0;
     for (int d = 0; d < p.n_lin; ++d) {
+        if (!p.lin[d].Qx) {
+            p.lin[d].Qx = p.Qx;
+            p.lin[d].s_x = p.s_x;
+        }
         // a SwiGLU pair spends two tile columns per output column
         const int64_t cols = p.lin[d].glu ? 2 * p.lin[d].N : p.lin[d].N;
         p.lin[d].tiles_n = (int)((cols + BN - 1) / BN);

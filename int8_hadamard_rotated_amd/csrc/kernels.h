@@ -61,6 +61,8 @@ constexpr int kMaxLinears = 16;
 enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
 
 struct GemmLinear {
+    const int8_t *Qx;    // [M][K] codes this linear reads (row stride K); null: GemmProblem's
+    const float *s_x;    // [M] their row scales (with Qx)
     const int8_t *Qw;    // [N][K]
     const float *s_w;    // [N] or null
     const float *bias;   // [N] or null
@@ -84,7 +86,7 @@ struct GemmLinear {
 };
 
 struct GemmProblem {
-    const int8_t *Qx;    // [M][K], row stride K
+    const int8_t *Qx;    // [M][K], row stride K: the input of every linear whose own Qx is null
     const float *s_x;    // [M]
     int64_t M;
     int64_t K;

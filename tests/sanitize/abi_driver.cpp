@@ -169,9 +169,18 @@ static void shared_and_grouped()
     const size_t ws = convrot_workspace_bytes(257, 768, 2);
     reset();
     EXPECT(convrot_int8_linear_shared(at(0), CONVROT_BF16, 257, 768, 768, 256, 3, d, at(100), ws, nullptr) == CONVROT_OK);
-    EXPECT(g_log.quantize_calls == 2 && g_log.gemm_calls == 2);
+    EXPECT(g_log.quantize_calls == 2 && g_log.gemm_calls == 1);
     EXPECT(g_log.q_alpha == 0.3f);                       // the last pass
-    EXPECT(g_log.gemm.n_lin == 1 && g_log.gemm.lin[0].alpha == 0.3f);
+    // one launch: the first two linears read the alpha = 1 tensor, the third its own
+    EXPECT(g_log.gemm.n_lin == 3 && g_log.gemm.lin[1].alpha == 1.0f && g_log.gemm.lin[2].alpha == 0.3f);
+    EXPECT(g_log.gemm.lin[0].Qx == at_t<const int8_t>(100) && g_log.gemm.lin[1].Qx == g_log.gemm.lin[0].Qx);
+    EXPECT(g_log.gemm.lin[2].Qx == at_t<const int8_t>(100) + convrot_workspace_bytes(257, 768, 1));
+    EXPECT(g_log.gemm.lin[2].s_x != nullptr && g_log.gemm.lin[2].s_x != g_log.gemm.lin[0].s_x);
+    convrot_linear_desc named[2] = {desc(32, 200, 96, 1.0f), desc(40, 300, 64, 1.0f)};
+    named[1].Qx = at_t<const int8_t>(500);
+    named[1].s_x = at_t<const float>(520);
+    EXPECT(convrot_int8_linear_shared(at(0), CONVROT_BF16, 257, 768, 768, 256, 2, named, at(100), ws, nullptr) ==
+           CONVROT_EINVAL);
     EXPECT(convrot_int8_linear_shared(at(0), CONVROT_BF16, 257, 768, 768, 256, 3, d, at(100), ws - 1, nullptr) ==
            CONVROT_EWORKSPACE);
     EXPECT(convrot_int8_linear_shared(at(0), CONVROT_BF16, 257, 768, 768, 256, 0, d, at(100), ws, nullptr) == CONVROT_EINVAL);
@@ -183,6 +192,17 @@ static void shared_and_grouped()
     EXPECT(g_log.gemm.lin[1].alpha == 0.5f && g_log.gemm.lin[2].alpha == 0.3f);
     convrot_linear_desc clash[2] = {desc(32, 200, 96, 1.0f), desc(40, 200, 64, 1.0f)};
     EXPECT(int8_linear_grouped(at_t<const int8_t>(0), at_t<const float>(16), 257, 768, 2, clash, nullptr) == CONVROT_EOVERLAP);
+    // a linear with its own quantized input
+    reset();
+    EXPECT(int8_linear_grouped(at_t<const int8_t>(0), at_t<const float>(16), 257, 768, 2, named, nullptr) == CONVROT_OK);
+    EXPECT(g_log.gemm_calls == 1 && g_log.gemm.n_lin == 2);
+    EXPECT(g_log.gemm.lin[0].Qx == at_t<const int8_t>(0) && g_log.gemm.lin[0].s_x == at_t<const float>(16));
+    EXPECT(g_log.gemm.lin[1].Qx == at_t<const int8_t>(500) && g_log.gemm.lin[1].s_x == at_t<const float>(520));
+    named[1].s_x = nullptr;
+    EXPECT(int8_linear_grouped(at_t<const int8_t>(0), at_t<const float>(16), 257, 768, 2, named, nullptr) == CONVROT_EINVAL);
+    named[1].s_x = at_t<const float>(520);
+    named[0].Y = at(500);                               // an output on the other linear's codes
+    EXPECT(int8_linear_grouped(at_t<const int8_t>(0), at_t<const float>(16), 257, 768, 2, named, nullptr) == CONVROT_EOVERLAP);
 
     reset();
     EXPECT(convrot_int8_linear_noalloc(at(0), CONVROT_BF16, 4096, 3072, 3072, 256, 1.0f, at_t<const int8_t>(32),

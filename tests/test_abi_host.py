@@ -302,6 +302,9 @@ def test_shared_validation(lib):
     assert shared(lib, good, ws=BASE) == EOVL                               # workspace hits X
     assert shared(lib, [desc(W1, Y1, a=-1.0)]) == EINVAL
     assert shared(lib, good, G=2) == EUNSUP
+    named = desc(W2, Y2)
+    named.Qx, named.s_x = BASE + 192 * MB, BASE + 200 * MB
+    assert shared(lib, [desc(W1, Y1), named]) == EINVAL                     # the entry quantizes X itself
     assert shared(lib, good, M=0) == OK
 
 
@@ -343,6 +346,18 @@ def test_grouped_validation(lib):
     assert call([desc(W1, Y1, a=0.0)]) == EINVAL
     assert call([desc(W1, Y1, ld=16)]) == EINVAL                       # ldy < N
     assert call(good, qx=0) == EINVAL
+
+    def own(W, Y, qx, sx):                                             # a linear with its own input
+        d = desc(W, Y)
+        d.Qx, d.s_x = qx, sx
+        return d
+    Qx2, sx2 = BASE + 32 * MB, BASE + 48 * MB
+    assert call([desc(W1, Y1), own(W2, Y2, Qx2, None)]) == EINVAL     # codes without scales
+    assert call([desc(W1, Y1), own(W2, Y2, None, sx2)]) == EINVAL     # scales without codes
+    assert call([desc(W1, Y1), own(W2, Y2, Qx2 + 8, sx2)]) == EINVAL  # codes not 16-byte aligned
+    assert call([desc(W1, Y1), own(W2, Y2, Qx2, sx2 + 2)]) == EINVAL  # scales not 4-byte aligned
+    assert call([desc(W1, Qx2 + 64), own(W2, Y2, Qx2, sx2)]) == EOVL  # output on another's codes
+    assert call([desc(W1, sx2), own(W2, Y2, Qx2, sx2)]) == EOVL       # output on another's scales
     assert call(good, M=0) == OK
 
 

@@ -158,6 +158,59 @@ def test_int8_linear_grouped(orc, M, K, Ns):
     assert np.all(host(wide)[:, Ns[2]:] == -7.0), "wrote past N"
 
 
+@pytest.mark.parametrize("M,K,Ns", [(515, 768, (130, 64, 257)), (1030, 512, (3072, 3072, 3072))])
+def test_int8_linear_grouped_own_inputs(orc, M, K, Ns):
+    """Linears of one launch reading different packed tensors: the pages'
+    path for two input scales (a quantization pass per scale, the division by
+    it in the reconstruction).  The second shape is 180 tiles of 256 x 256:
+    the kernel with the division compiled in, which its alpha = 1 tiles skip."""
+    rng = np.random.default_rng(M + 7 * K)
+    G = 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    alphas = (1.0, 0.3, 1.0)
+    packs = {a: orc.quantize_rows(X, G, a, threads=THREADS) for a in set(alphas)}
+    dpacks = {a: (dev(p.q), dev(p.s)) for a, p in packs.items()}
+    lins, wants = [], []
+    for N, a in zip(Ns, alphas):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        A = orc.gemm_i32(packs[a].q, Qw, threads=THREADS)
+        wants.append(orc.epilogue(A, packs[a].s, sw, b, a, oracle.F32, threads=THREADS))
+        lin = dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=oracle.F32)
+        if a != 1.0:
+            lin["Qx"], lin["s_x"] = dpacks[a]
+        lins.append(lin)
+    say("int8_linear_grouped own inputs", M, K, Ns)
+    qx, sx = dpacks[1.0]
+    outs = cr.int8_linear_grouped(qx, sx, lins)
+    for j, (y, want) in enumerate(zip(outs, wants)):
+        assert_bits_equal(host(y), want, f"grouped linear {j} alpha={alphas[j]}")
+
+
+def test_shared_mixed_scales_big_grid(orc):
+    """convrot_int8_linear_shared with alpha = 1 and alpha = 0.3 linears: two
+    quantization passes, then one grouped launch of 180 tiles of 256 x 256
+    over both packed tensors (the division kernel, skipped on the alpha = 1
+    tiles), against the oracle's literal path."""
+    import torch
+    rng = np.random.default_rng(77)
+    M, K, G = 1030, 512, 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.F32)
+    alphas, Ns = (1.0, 0.3, 1.0), (3072, 3072, 3072)
+    preps, lins = [], []
+    for a, N in zip(alphas, Ns):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        preps.append((Qw, sw, b))
+        lins.append(dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=oracle.F32))
+    ws = torch.empty(cr.convrot_workspace_bytes(M, K, 2), dtype=torch.uint8, device="cuda:0")
+    say("shared mixed scales", M, K, Ns)
+    outs = [host(y) for y in cr.convrot_int8_linear_shared(dev_x(X), G, lins, workspace=ws)]
+    for (Qw, sw, b), a, y in zip(preps, alphas, outs):
+        want = orc.linear(X, G, Qw, sw, b, a, oracle.F32, threads=THREADS)
+        assert_bits_equal(y, want, f"alpha={a}")
+
+
 def test_int8_linear_strided_output(orc):
     """ldy > N, and an output whose rows do not allow vector stores."""
     rng = np.random.default_rng(5)
