@@ -58,15 +58,16 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def quantize_bytes(w: workloads.Workload) -> int:
-    """Algorithmic bytes of one quantize pass: read X once (and the producer's
-    inputs, if any: the gated activation's second tensor, the RMSNorm weight,
-    the Modulate scale and shift), write the packed tensor."""
+def quantize_bytes(w: workloads.Workload, n_scales: int = 1) -> int:
+    """Algorithmic bytes of the quantization of one step: read X once (and
+    the producer's inputs, if any: the gated activation's second tensor, the
+    RMSNorm weight, the Modulate scale and shift), write the packed tensor of
+    each of the n_scales input scales."""
     esz = 2 if w.x_dtype == workloads.BF16 else 4
     m_pad = (w.M + 3) // 4 * 4
     mod = (8 * w.K if w.modulate else 0) + (4 * w.K if w.rmsnorm else 0)
     up = w.M * w.K * esz if w.glu else 0
-    return w.M * w.K * esz + up + m_pad * w.K + 4 * m_pad + mod
+    return w.M * w.K * esz + up + n_scales * (m_pad * w.K + 4 * m_pad) + mod
 
 
 def gemm_ops(w: workloads.Workload, n_linears: int) -> int:
@@ -336,7 +337,8 @@ def main() -> int:
             if k:
                 c["Qx"], c["s_x"] = views[k]
             calls.append(c)
-        sets.append(dict(X=Xd, up=up, ws=ws, Y=Ys, lins=ls, views=views, calls=calls))
+        slots = [ws[k * slot:(k + 1) * slot] for k in range(n_packed)]
+        sets.append(dict(X=Xd, up=up, ws=ws, Y=Ys, lins=ls, views=views, calls=calls, slots=slots))
     torch.cuda.synchronize()
 
     mod = (cr.Modulate(torch.from_numpy(inp.mod_scale).to(dev), torch.from_numpy(inp.mod_shift).to(dev))
@@ -347,15 +349,21 @@ def main() -> int:
     gate = torch.from_numpy(inp.gate).to(dev) if w.gated else None
     slot = cr.convrot_workspace_bytes(w.M, w.K, 1)
 
-    def quantize(i, k=0):
+    def quantize(i):
+        """The step's quantization: one pass per input scale (plain rows of
+        several scales in one call, which reads binary32 X once)."""
         S = sets[i % n_sets]
-        ws = S["ws"][k * slot:(k + 1) * slot]
-        if w.glu:
-            cr.convrot_quantize_rows_pre(S["X"], cr.GatedAct(S["up"], w.glu), w.G, scales[k], packed=ws)
-        elif mod is not None:
-            cr.convrot_quantize_rows_pre(S["X"], mod, w.G, scales[k], packed=ws)
-        else:
-            cr.convrot_quantize_rows(S["X"], w.G, scales[k], packed=ws)
+        if n_packed > 1 and mod is None and not w.glu:
+            cr.convrot_quantize_rows_scales(S["X"], w.G, scales, packed=S["slots"])
+            return
+        for k in range(n_packed):
+            ws = S["slots"][k]
+            if w.glu:
+                cr.convrot_quantize_rows_pre(S["X"], cr.GatedAct(S["up"], w.glu), w.G, scales[k], packed=ws)
+            elif mod is not None:
+                cr.convrot_quantize_rows_pre(S["X"], mod, w.G, scales[k], packed=ws)
+            else:
+                cr.convrot_quantize_rows(S["X"], w.G, scales[k], packed=ws)
 
     def gemm(i):
         """The step's GEMM launch: every linear, each reading the packed tensor
@@ -378,11 +386,10 @@ def main() -> int:
             lin_fn(qx, sx, l["Qw"], l["s_w"], l["bias"], l["input_scale"], Y=l["Y"], M=w.M)
 
     def step(i):
-        # one quantize pass per distinct input scale, then one GEMM launch over
-        # every linear (the launches of the shared entry, without folding a
-        # power-of-two scale into the alpha = 1 pass)
-        for k in range(n_packed):
-            quantize(i, k)
+        # the quantization of every distinct input scale, then one GEMM launch
+        # over every linear (the launches of the shared entry, without folding
+        # a power-of-two scale into the alpha = 1 pass)
+        quantize(i)
         gemm(i)
 
     def step_folded(i):
@@ -472,17 +479,19 @@ def main() -> int:
                            "256 MiB Infinity Cache"},
         "step_us_events": round(ev_step_us, 3),
     }
-    # per-kernel figures: the quantize pass of the first packed tensor and the
-    # step's GEMM launch (for qkv: the grouped launch of all four linears over
-    # both packed tensors), each launched K times back to back
+    # per-kernel figures: the step's quantization (for qkv: one pass for both
+    # input scales) and the step's GEMM launch (for qkv: the grouped launch of
+    # all four linears over both packed tensors), each launched K times back
+    # to back
     tq = kernel_us(quantize) * 1e-6
     tg = kernel_us(gemm) * 1e-6
     g_ops = gemm_ops(w, 2 if w.swiglu else w.n_linears)
-    q_gbs = quantize_bytes(w) / tq / 1e9
+    q_bytes = quantize_bytes(w, n_packed)
+    q_gbs = q_bytes / tq / 1e9
     g_tops = g_ops / tg / 1e12
     rec["quantize"] = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-                       "us": round(tq * 1e6, 3), "bytes": quantize_bytes(w),
+                       "us": round(tq * 1e6, 3), "bytes": q_bytes,
                        "traffic": measured_traffic("quantize", w.name),
                        "single_launch_us": kernel_spread(quantize)}
     rec["roofline"] = {"bound": "mfma", "achieved": round(g_tops, 1), "peak": INT8_PEAK_TOPS,
@@ -496,15 +505,14 @@ def main() -> int:
                        "note": "int8 ops: one multiply-add counts as 2",
                        "single_launch_us": kernel_spread(gemm)}
     if n_packed > 1:
-        rec["quantize"]["passes"] = {
-            "what": f"{n_packed} passes per step, one per input scale {scales}; figures above "
-                    "are the first's (the others move the same bytes)",
-            "us_per_step": round(n_packed * tq * 1e6, 3)}
+        rec["quantize"]["scales"] = (
+            f"input scales {scales}: one convrot_quantize_rows_scales call writes a packed tensor "
+            "for each, reading X once; bytes count X once and every packed tensor")
     # the quantize pass against a plain copy of the same bytes: the probe
     # kernel reads X ([M, K], bf16 or binary32) with 16-byte loads and writes
     # one byte per element with 16-byte stores, no arithmetic, back to back
     # over the same input sets
-    if not w.glu and not args.no_probe:
+    if not w.glu and not args.no_probe and n_packed == 1:
         probe = probe_library()
         esz = 2 if w.x_dtype == workloads.BF16 else 4
         dst = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)

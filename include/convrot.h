@@ -106,6 +106,20 @@ size_t convrot_packed_bytes(int64_t M, int64_t K);
 int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                           int group_size, float input_scale, void *packed, void *stream);
 
+/* convrot_quantize_rows for several input scales of the same X (page "INT8
+ * Convrot Safetensors", section "How INT8 convrot works": each input scale
+ * other than 1 gets its own quantization of X, pre-scaled by it): packed[i]
+ * receives exactly the bytes of convrot_quantize_rows(..., input_scales[i],
+ * packed[i], ...).  Binary32 rows whose workgroups stay within 256 threads
+ * (K up to 16 384 with G = 256) are read from HBM once per two scales;
+ * other rows are read once per scale.  input_scales and packed are host
+ * arrays of n entries, 1 <= n <= 16; each packed[i] is a device buffer of
+ * convrot_packed_bytes(M, K), 16-byte aligned, overlapping neither X nor
+ * another packed[k] (CONVROT_EOVERLAP). */
+int convrot_quantize_rows_scales(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 int group_size, int n, const float *input_scales,
+                                 void *const *packed, void *stream);
+
 /* INT8 linear on already-quantized activations, the GEMM + reconstruction
  * (page "INT8 Convrot Safetensors", section "How INT8 convrot works": the
  * int32 accumulation and Y = A s_x s_w + b; page "ggml operator extensions",

@@ -149,6 +149,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
     sigs = {
         "convrot_packed_bytes": (sz, [i64, i64]),
         "convrot_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, vp]),
+        "convrot_quantize_rows_scales": (i32, [vp, i32, i64, i64, i64, i32, i32, vp, vp, vp]),
         "convrot_quantize_rows_pre": (i32, [vp, i32, i64, i64, i64, ctypes.POINTER(PreDesc), i32,
                                             f32, vp, vp]),
         "int8_linear": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, f32, vp, i32, i64, vp]),
@@ -263,6 +264,24 @@ def convrot_quantize_rows(X, group_size: int, input_scale: float = 1.0, packed=N
     rc = library().convrot_quantize_rows(_ptr(X), _dtype_code(X), M, K, ldx, group_size,
                                          ctypes.c_float(input_scale), _ptr(packed), _stream(stream, X))
     _check("convrot_quantize_rows", rc)
+    return packed
+
+
+def convrot_quantize_rows_scales(X, group_size: int, input_scales, packed=None, stream=None):
+    """convrot_quantize_rows for several input scales of the same X in one
+    call; returns the packed tensors (allocated where ``packed`` is None)."""
+    torch = _torch()
+    M, K = X.shape
+    ldx = _row_stride(X) if M > 0 else K
+    n = len(input_scales)
+    if packed is None:
+        packed = [torch.empty(convrot_packed_bytes(M, K), dtype=torch.uint8, device=X.device)
+                  for _ in range(n)]
+    scales = (ctypes.c_float * max(n, 1))(*[float(a) for a in input_scales])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(p) for p in packed])
+    rc = library().convrot_quantize_rows_scales(_ptr(X), _dtype_code(X), M, K, ldx, group_size, n,
+                                                scales, ptrs, _stream(stream, X))
+    _check("convrot_quantize_rows_scales", rc)
     return packed
 
 

@@ -302,6 +302,37 @@ int convrot_quantize_rows(const void *X, int x_dtype, int64_t M, int64_t K, int6
                                      packed, stream);
 }
 
+int convrot_quantize_rows_scales(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 int group_size, int n, const float *input_scales,
+                                 void *const *packed, void *stream)
+{
+    if (n < 1 || n > kMaxLinears || !input_scales || !packed)
+        return CONVROT_EINVAL;
+    for (int i = 0; i < n; ++i) {
+        const int rc = check_quantize_args(X, x_dtype, M, K, ldx, group_size, input_scales[i]);
+        if (rc != CONVROT_OK)
+            return rc;
+    }
+    if (M == 0)
+        return CONVROT_OK;
+    const int64_t pb = (int64_t)convrot_packed_bytes(M, K);
+    const Span xs = rows_span(X, M, K, ldx, elem_bytes(x_dtype));
+    for (int i = 0; i < n; ++i) {
+        if (!packed[i] || !aligned(packed[i], 16))
+            return CONVROT_EINVAL;
+        const Span out = span_of(packed[i], pb);
+        if (overlap(xs, out))
+            return CONVROT_EOVERLAP;
+        for (int k = 0; k < i; ++k) {
+            if (overlap(out, span_of(packed[k], pb)))
+                return CONVROT_EOVERLAP;
+        }
+    }
+    (void)hipGetLastError();
+    return hip_status(launch_quantize_scales(X, x_dtype, M, K, ldx, group_size, n, input_scales,
+                                             packed, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {
@@ -669,11 +700,23 @@ int shared_impl(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int8_t *base = static_cast<int8_t *>(workspace);
-    for (int s = 0; s < n_slots; ++s) {
-        rc = hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, scales[s], op,
-                                        base + s * slot_bytes, st));
+    if (op.kind == kPreNone) {
+        // plain rows: the passes of every scale together (binary32 rows are
+        // then read once per few scales)
+        void *outs[kMaxLinears];
+        for (int s = 0; s < n_slots; ++s)
+            outs[s] = base + s * slot_bytes;
+        rc = hip_status(launch_quantize_scales(X, x_dtype, M, K, ldx, group_size, n_slots, scales,
+                                               outs, st));
         if (rc != CONVROT_OK)
             return rc;
+    } else {
+        for (int s = 0; s < n_slots; ++s) {
+            rc = hip_status(launch_quantize(X, x_dtype, M, K, ldx, group_size, scales[s], op,
+                                            base + s * slot_bytes, st));
+            if (rc != CONVROT_OK)
+                return rc;
+        }
     }
     // one grouped launch: every linear reads the packed tensor of its scale
     const int64_t m_pad = round_up(M, 4);

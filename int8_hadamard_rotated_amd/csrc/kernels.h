@@ -55,6 +55,20 @@ hipError_t launch_expf(const float *x, float *y, int64_t n, hipStream_t stream);
 hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
                            float alpha, const PreOp &pre, void *packed, hipStream_t stream);
 
+// Several input scales of one X without a producer: packed[i] receives the
+// bytes of launch_quantize with alpha[i].  Binary32 rows that the staged
+// kernel takes are read once per kMaxPassScales scales; other rows get one
+// pass per scale.
+constexpr int kMaxPassScales = 2;
+struct ScaleOuts {
+    int n;
+    float alpha[kMaxPassScales];
+    int8_t *Q[kMaxPassScales];
+    float *S[kMaxPassScales];
+};
+hipError_t launch_quantize_scales(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                                  int n, const float *alpha, void *const *packed, hipStream_t stream);
+
 // ------------------------------------------------------------------- GEMM
 constexpr int kMaxLinears = 16;
 

@@ -728,12 +728,21 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024) void quantize_rows_
 // compiler's order (wave_lds_sync).  Odd quads store their pieces with the slot index
 // XOR-ed by one (codes: by 4 * (quad % 4)) so that the lanes of one read
 // instruction spread over distinct LDS banks.
-template <int G, int NC, bool SCALED, int MOD>
+//
+// NS = 2: one pass for two input scales (no producer).  The rows are loaded
+// and staged once; every lane scales and rotates its chunks for both scales
+// in registers, the row maxima of both meet at one barrier, and the codes of
+// each scale go out in turn through the staging region.  Each scale's bytes
+// are those of its own pass.
+template <int G, int NC, bool SCALED, int MOD, int NS = 1>
 __global__ __launch_bounds__(256) void quantize_rows_staged(
     const float *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
     const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
-    int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg)
+    int8_t *__restrict__ Q, float *__restrict__ S, int quads_per_row, int rows_per_wg,
+    ScaleOuts outs)
 {
+    constexpr bool MULTI = NS > 1;
+    static_assert(NS == 1 || (NS == 2 && MOD == 0 && !SCALED), "two scales: plain rows, scales in outs");
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
     static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
     constexpr int kPC = 2;                                // 16-B pieces per 8-element chunk
@@ -743,7 +752,7 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     constexpr int kOutPieces = 16 * (32 * NC / 16);      // 16-B code pieces per wave
     constexpr int kStoresPerLane = kOutPieces / 64;      // = NC / 2
     extern __shared__ __attribute__((aligned(16))) unsigned char stage_lds[];
-    __shared__ unsigned row_max[256];
+    __shared__ unsigned row_max[NS * 256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int quad = tid >> 2;
@@ -754,11 +763,15 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     const int64_t row = row0 + row_local;
     const bool live = row < M;
+    constexpr int kQuadOut = 32 * NC / 16;                      // 16-B code pieces per quad
     unsigned char *wst = stage_lds + wave * (kWavePieces * 16);
     constexpr int kFlip = 1;
 
-    if (tid < rows_per_wg)
-        row_max[tid] = 0u;
+    if (tid < rows_per_wg) {
+#pragma unroll
+        for (int a = 0; a < NS; ++a)
+            row_max[256 * a + tid] = 0u;
+    }
 
     // contiguous loads: lane L, instruction i takes wave piece p = 64 i + L
     using Raw = v4u;
@@ -785,7 +798,7 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     __syncthreads();   // row_max cleared (the staging region is wave-private)
 
     const int ql_me = (tid >> 2) & 15;                          // my quad within the wave
-    float v[NC][8];
+    float v[NS][NC][8];
     if (live) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -800,65 +813,82 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
                 const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    v[c][4 * h + t] = __builtin_bit_cast(float, w[t]);
+                    v[0][c][4 * h + t] = __builtin_bit_cast(float, w[t]);
             }
         }
         const int64_t span_me = (int64_t)q_in_row * (32 * NC);
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            modulate8<MOD>(v[c], mod_scale, mod_shift, span_me + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1));
-
-        if constexpr (SCALED) {
+            modulate8<MOD>(v[0][c], mod_scale, mod_shift, span_me + 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1));
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
+        for (int a = NS - 1; a >= 0; --a) {
+            const float alpha_a = MULTI ? outs.alpha[a] : alpha;
+            if (SCALED || (MULTI && alpha_a != 1.0f)) {
 #pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    v[c][p] = v[c][p] * alpha;
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        v[a][c][p] = v[0][c][p] * alpha_a;
+            } else if (a > 0) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        v[a][c][p] = v[0][c][p];
+            }
+            rotate_span<G, NC, MOD == 0>(v[a]);
+            const float m = quad_abs_max<NC>(v[a]);
+            if ((tid & 3) == 0)
+                atomicMax(&row_max[256 * a + row_local], __builtin_bit_cast(unsigned, m));
         }
-        rotate_span<G, NC, MOD == 0>(v);
-        const float m = quad_abs_max<NC>(v);
-        if ((tid & 3) == 0)
-            atomicMax(&row_max[row_local], __builtin_bit_cast(unsigned, m));
     }
     __syncthreads();
 
-    // codes: 8 bytes per chunk into the wave's staging region (32 NC bytes per
-    // quad), then contiguous 16-B stores
-    constexpr int kQuadOut = 32 * NC / 16;                      // 16-B code pieces per quad
-    if (row < M_pad) {
-        unsigned char *qst = wst + 16 * ql_me * kQuadOut;
-        if (!live) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int o = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
-                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = v2u{0u, 0u};
-            }
-            if (q_in_row == 0 && (tid & 3) == 0)
-                S[row] = 0.0f;
-        } else {
-            const float m = __builtin_bit_cast(float, row_max[row_local]);
-            const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
-            if (q_in_row == 0 && (tid & 3) == 0)
-                S[row] = __fdiv_rn(m, 127.0f);
+    for (int a = 0; a < NS; ++a) {
+        int8_t *const Qa = MULTI ? outs.Q[a] : Q;
+        float *const Sa = MULTI ? outs.S[a] : S;
+        if constexpr (MULTI) {
+            if (a > 0)
+                wave_lds_sync();   // these codes reuse the region the last stores read
+        }
+        // codes: 8 bytes per chunk into the wave's staging region (32 NC bytes
+        // per quad), then contiguous 16-B stores
+        if (row < M_pad) {
+            unsigned char *qst = wst + 16 * ql_me * kQuadOut;
+            if (!live) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int o = chunk_offset(j0, j1, c);
-                *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = encode8(v[c], inv);
+                for (int c = 0; c < NC; ++c) {
+                    const int o = 8 * j0 + 16 * (c & 1) + 32 * j1 + 64 * (c >> 1);
+                    *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = v2u{0u, 0u};
+                }
+                if (q_in_row == 0 && (tid & 3) == 0)
+                    Sa[row] = 0.0f;
+            } else {
+                const float m = __builtin_bit_cast(float, row_max[256 * a + row_local]);
+                const float inv = m > 0.0f ? __fdiv_rn(127.0f, m) : 0.0f;
+                if (q_in_row == 0 && (tid & 3) == 0)
+                    Sa[row] = __fdiv_rn(m, 127.0f);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int o = chunk_offset(j0, j1, c);
+                    *reinterpret_cast<v2u *>(qst + 16 * ((o >> 4) ^ (4 * (ql_me & 3) % kQuadOut)) + (o & 15)) = encode8(v[a][c], inv);
+                }
             }
         }
-    }
-    wave_lds_sync();   // lanes store pieces other lanes staged
+        wave_lds_sync();   // lanes store pieces other lanes staged
 #pragma unroll
-    for (int i = 0; i < kStoresPerLane; ++i) {
-        const int p = 64 * i + lane;                            // wave code piece
-        const int ql = p / kQuadOut, pi = p % kQuadOut;
-        const int qw = 16 * wave + ql;
-        int rl, qi;
-        quad_place<MOD>(qw, quads_per_row, rows_per_wg, rl, qi);
-        const int64_t r = row0 + rl;
-        if (qw < n_quads && r < M_pad) {
-            const v4u val = *reinterpret_cast<const v4u *>(wst + 16 * (ql * kQuadOut + (pi ^ (4 * (ql & 3) % kQuadOut))));
-            *reinterpret_cast<v4u *>(Q + r * K + (int64_t)qi * (32 * NC) + 16 * pi) = val;
+        for (int i = 0; i < kStoresPerLane; ++i) {
+            const int p = 64 * i + lane;                            // wave code piece
+            const int ql = p / kQuadOut, pi = p % kQuadOut;
+            const int qw = 16 * wave + ql;
+            int rl, qi;
+            quad_place<MOD>(qw, quads_per_row, rows_per_wg, rl, qi);
+            const int64_t r = row0 + rl;
+            if (qw < n_quads && r < M_pad) {
+                const v4u val = *reinterpret_cast<const v4u *>(wst + 16 * (ql * kQuadOut + (pi ^ (4 * (ql & 3) % kQuadOut))));
+                *reinterpret_cast<v4u *>(Qa + r * K + (int64_t)qi * (32 * NC) + 16 * pi) = val;
+            }
         }
     }
 }
@@ -876,10 +906,23 @@ hipError_t launch_staged(const float *X, int64_t M, int64_t K, int64_t ldx, floa
     const int64_t blocks = (m_pad + rows - 1) / rows;
     if (alpha != 1.0f)
         hipLaunchKernelGGL((quantize_rows_staged<G, NC, true, MOD>), dim3((unsigned)blocks), dim3(threads), lds,
-                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows);
+                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows, ScaleOuts{});
     else
         hipLaunchKernelGGL((quantize_rows_staged<G, NC, false, MOD>), dim3((unsigned)blocks), dim3(threads), lds,
-                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows);
+                           stream, X, M, m_pad, K, ldx, alpha, pre.scale, pre.shift, Q, S, qr, rows, ScaleOuts{});
+    return hipGetLastError();
+}
+
+// Two scales in one staged pass (binary32 rows, no producer).
+template <int G, int NC>
+hipError_t launch_staged_scales(const float *X, int64_t M, int64_t K, int64_t ldx, const ScaleOuts &outs,
+                                int64_t m_pad, int qr, int rows, hipStream_t stream)
+{
+    const int threads = 4 * qr * rows;
+    const size_t lds = (size_t)((threads + 63) / 64) * kStagedWaveBytes<NC>;
+    const int64_t blocks = (m_pad + rows - 1) / rows;
+    hipLaunchKernelGGL((quantize_rows_staged<G, NC, false, 0, 2>), dim3((unsigned)blocks), dim3(threads), lds,
+                       stream, X, M, m_pad, K, ldx, 1.0f, nullptr, nullptr, nullptr, nullptr, qr, rows, outs);
     return hipGetLastError();
 }
 
@@ -893,6 +936,18 @@ int gcd_int(int a, int b)
     return a;
 }
 
+// Rows per workgroup for qr quads per row: the smallest row count that fills
+// whole waves, then grown towards 256 threads.
+int plan_rows(int qr, int max_threads)
+{
+    int rows = 16 / gcd_int(qr, 16);
+    if (4 * qr * rows > max_threads)
+        rows = max_threads / (4 * qr) > 0 ? max_threads / (4 * qr) : 1;
+    while (4 * qr * rows * 2 <= 256)
+        rows *= 2;
+    return rows;
+}
+
 template <typename XT, int G, int NC, int MOD, bool RMS, int ACT>
 hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                   void *packed, hipStream_t stream)
@@ -900,12 +955,7 @@ hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float 
     const int64_t m_pad = (M + 3) / 4 * 4;
     const int qr = (int)(K / (32 * NC));
     constexpr int kMaxThreads = (RMS || ACT != 0) ? 512 : 1024;
-    // smallest row count that fills whole waves, then grow towards 256 threads
-    int rows = 16 / gcd_int(qr, 16);
-    if (4 * qr * rows > kMaxThreads)
-        rows = kMaxThreads / (4 * qr) > 0 ? kMaxThreads / (4 * qr) : 1;
-    while (4 * qr * rows * 2 <= 256)
-        rows *= 2;
+    const int rows = plan_rows(qr, kMaxThreads);
     int threads = 4 * qr * rows;
     // the gated activation doubles the threads of its activation pass where
     // the launch bounds allow (the quad layout keeps 4 * qr * rows of them)
@@ -1052,6 +1102,63 @@ hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int
     if (x_dtype == 0)
         return launch_pre<float>(G, X, M, K, ldx, alpha, pre, packed, stream);
     return launch_pre<uint16_t>(G, X, M, K, ldx, alpha, pre, packed, stream);
+}
+
+namespace {
+
+template <int NC>
+hipError_t launch_scales_nc(int G, const float *X, int64_t M, int64_t K, int64_t ldx, const ScaleOuts &outs,
+                            int64_t m_pad, int qr, int rows, hipStream_t stream)
+{
+    switch (G) {
+    case 4: return launch_staged_scales<4, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
+    case 16: return launch_staged_scales<16, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
+    case 64: return launch_staged_scales<64, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
+    default:
+        if constexpr (NC == 8)
+            return launch_staged_scales<256, 8>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
+        return hipErrorInvalidValue;   // not reached: G = 256 comes with K % 256 == 0
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_scales(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                                  int n, const float *alpha, void *const *packed, hipStream_t stream)
+{
+    // the staged kernel's rows: binary32 with at most 256 threads per
+    // workgroup (the choice launch_typed makes for plain rows)
+    const int nc = K % 256 == 0 ? 8 : K % 128 == 0 ? 4 : 2;
+    const int qr = (int)(K / (32 * nc));
+    const int rows = plan_rows(qr, 1024);
+    const bool staged = x_dtype == 0 && 4 * qr * rows <= 256;
+    if (!staged || n < 2) {
+        for (int i = 0; i < n; ++i) {
+            const hipError_t e = launch_quantize(X, x_dtype, M, K, ldx, G, alpha[i], PreOp{}, packed[i], stream);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    const int64_t m_pad = (M + 3) / 4 * 4;
+    for (int i0 = 0; i0 < n; i0 += kMaxPassScales) {
+        if (n - i0 == 1)      // an odd scale left over: its own pass
+            return launch_quantize(X, x_dtype, M, K, ldx, G, alpha[i0], PreOp{}, packed[i0], stream);
+        ScaleOuts outs{};
+        outs.n = kMaxPassScales;
+        for (int a = 0; a < outs.n; ++a) {
+            outs.alpha[a] = alpha[i0 + a];
+            outs.Q[a] = static_cast<int8_t *>(packed[i0 + a]);
+            outs.S[a] = reinterpret_cast<float *>(outs.Q[a] + m_pad * K);
+        }
+        const float *Xf = static_cast<const float *>(X);
+        const hipError_t e = nc == 8 ? launch_scales_nc<8>(G, Xf, M, K, ldx, outs, m_pad, qr, rows, stream)
+                             : nc == 4 ? launch_scales_nc<4>(G, Xf, M, K, ldx, outs, m_pad, qr, rows, stream)
+                                       : launch_scales_nc<2>(G, Xf, M, K, ldx, outs, m_pad, qr, rows, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace convrot_detail

@@ -170,6 +170,7 @@ static void shared_and_grouped()
     reset();
     EXPECT(convrot_int8_linear_shared(at(0), CONVROT_BF16, 257, 768, 768, 256, 3, d, at(100), ws, nullptr) == CONVROT_OK);
     EXPECT(g_log.quantize_calls == 2 && g_log.gemm_calls == 1);
+    EXPECT(g_log.scales_calls == 1 && g_log.q_n == 2);   // both scales in one quantization call
     EXPECT(g_log.q_alpha == 0.3f);                       // the last pass
     // one launch: the first two linears read the alpha = 1 tensor, the third its own
     EXPECT(g_log.gemm.n_lin == 3 && g_log.gemm.lin[1].alpha == 1.0f && g_log.gemm.lin[2].alpha == 0.3f);
@@ -203,6 +204,22 @@ static void shared_and_grouped()
     named[1].s_x = at_t<const float>(520);
     named[0].Y = at(500);                               // an output on the other linear's codes
     EXPECT(int8_linear_grouped(at_t<const int8_t>(0), at_t<const float>(16), 257, 768, 2, named, nullptr) == CONVROT_EOVERLAP);
+
+    // several input scales of one X
+    reset();
+    const float sc[3] = {1.0f, 0.5f, 0.3f};
+    const size_t pb = convrot_packed_bytes(257, 768);
+    void *outs[3] = {at(100), static_cast<char *>(at(100)) + pb, at(120)};
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 3, sc, outs, nullptr) == CONVROT_OK);
+    EXPECT(g_log.scales_calls == 1 && g_log.q_n == 3 && g_log.quantize_calls == 3 && g_log.q_packed == at(120));
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 0, sc, outs, nullptr) == CONVROT_EINVAL);
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 3, nullptr, outs, nullptr) == CONVROT_EINVAL);
+    void *overlapping[2] = {at(100), static_cast<char *>(at(100)) + pb - 16};
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 2, sc, overlapping, nullptr) == CONVROT_EOVERLAP);
+    void *on_x[1] = {at(0)};
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 1, sc, on_x, nullptr) == CONVROT_EOVERLAP);
+    const float bad[2] = {1.0f, 0.0f};
+    EXPECT(convrot_quantize_rows_scales(at(0), CONVROT_F32, 257, 768, 768, 256, 2, bad, outs, nullptr) == CONVROT_EINVAL);
 
     reset();
     EXPECT(convrot_int8_linear_noalloc(at(0), CONVROT_BF16, 4096, 3072, 3072, 256, 1.0f, at_t<const int8_t>(32),

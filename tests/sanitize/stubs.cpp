@@ -32,6 +32,17 @@ hipError_t launch_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int
     return hipSuccess;
 }
 
+hipError_t launch_quantize_scales(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int G,
+                                  int n, const float *alpha, void *const *packed, hipStream_t stream)
+{
+    // recorded as one call, and as the passes it stands for
+    g_log.scales_calls++;
+    g_log.q_n = n;
+    for (int i = 0; i < n; ++i)
+        launch_quantize(X, x_dtype, M, K, ldx, G, alpha[i], PreOp{}, packed[i], stream);
+    return hipSuccess;
+}
+
 hipError_t launch_gemm(GemmProblem p, hipStream_t)
 {
     g_log.gemm_calls++;

@@ -5,7 +5,7 @@
 namespace convrot_detail {
 
 struct StubLog {
-    int quantize_calls = 0, gemm_calls = 0, expf_calls = 0;
+    int quantize_calls = 0, gemm_calls = 0, expf_calls = 0, scales_calls = 0, q_n = 0;
     int64_t last_n = 0;
     const void *q_X = nullptr;
     int q_dtype = -1;

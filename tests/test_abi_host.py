@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
         "convrot_int8_linear", "convrot_int8_linear_shared", "convrot_int8_gemm_i32",
         "convrot_status_string", "convrot_quantize_rows_pre", "convrot_int8_linear_shared_pre",
         "int4_linear", "convrot_int4_gemm_i32", "int8_linear_post", "convrot_expf",
-        "int8_swiglu_linear", "convrot_int8_linear_noalloc", "int8_linear_grouped"])
+        "int8_swiglu_linear", "convrot_int8_linear_noalloc", "int8_linear_grouped",
+        "convrot_quantize_rows_scales"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -95,6 +96,30 @@ def test_quantize_validation(lib):
     assert q(lib, packed=BASE + 1024) == EOVL            # packed overlaps X
     assert q(lib, M=0) == OK                             # empty input: nothing enqueued
     assert q(lib, M=0, X=0, packed=0) == OK
+
+
+def test_quantize_scales_validation(lib):
+    """convrot_quantize_rows_scales: count, scales and the packed tensors'
+    placement, all before any HIP call."""
+    M, K = 8, 256
+    pb = cr.convrot_packed_bytes(M, K)
+
+    def call(scales, outs, n=None, X=BASE, G=16, M=M):
+        sc = (ctypes.c_float * max(len(scales), 1))(*scales)
+        ps = (ctypes.c_void_p * max(len(outs), 1))(*outs)
+        return lib.convrot_quantize_rows_scales(ctypes.c_void_p(X), cr.F32, M, K, K, G,
+                                                len(scales) if n is None else n, sc, ps, None)
+    P0, P1 = BASE + 64 * MB, BASE + 96 * MB
+    assert call([1.0, 0.5], [P0, P1], n=0) == EINVAL
+    assert call([1.0] * 17, [P0] * 17) == EINVAL
+    assert call([1.0, 0.0], [P0, P1]) == EINVAL          # a scale that is not positive
+    assert call([1.0, float("nan")], [P0, P1]) == EINVAL
+    assert call([1.0, 0.5], [P0, 0]) == EINVAL           # a missing packed tensor
+    assert call([1.0, 0.5], [P0, P1 + 8]) == EINVAL      # misaligned
+    assert call([1.0, 0.5], [P0, P0 + pb - 16]) == EOVL  # two packed tensors overlap
+    assert call([1.0, 0.5], [P0, BASE + 1024]) == EOVL   # a packed tensor on X
+    assert call([1.0, 0.5], [P0, P1], G=2) == EUNSUP
+    assert call([1.0, 0.5], [P0, P1], M=0) == OK
 
 
 def qpre(lib, kind=cr.PRE_MODULATE, sc=BASE + 96 * MB, sh=BASE + 97 * MB, M=8, K=256,

@@ -58,6 +58,40 @@ def test_edge_shapes(orc, G, dtype):
 
 
 
+# Several input scales of one X in one call: binary32 rows of the staged
+# kernel read X once per two scales (five scales: two such launches and one
+# single pass), other
+# rows (bf16; binary32 rows of 32 768 in the workgroup kernel) one pass per
+# scale.  Each packed tensor must equal its own pass byte for byte, pad rows
+# and scale tail included, and nothing past it may change.
+SCALES_CASES = [(4096, 3072, workloads.F32, 256, (1.0, 0.5)),
+                (129, 3072, workloads.F32, 256, (1.0, 0.3, 2.0 ** -20, 7.5, 0.5)),
+                (33, 1280, workloads.F32, 64, (0.3, 1.0, 0.25)),
+                (13, 512, workloads.F32, 16, (1.0, 0.5)),
+                (17, 192, workloads.F32, 4, (3.0, 1.0)),
+                (6, 8192, workloads.F32, 256, (1.0, 0.3)),
+                (3, 32768, workloads.F32, 256, (1.0, 0.3)),
+                (129, 3072, workloads.BF16, 256, (1.0, 0.5, 0.3))]
+
+
+@pytest.mark.parametrize("M,K,dtype,G,scales", SCALES_CASES)
+def test_quantize_rows_scales(orc, M, K, dtype, G, scales):
+    import torch
+    rng = np.random.default_rng(M + K + G)
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, dtype)
+    pb = cr.convrot_packed_bytes(M, K)
+    slot = (pb + 255) // 256 * 256 + 256
+    buf = torch.full((slot * len(scales),), 0x5A, dtype=torch.uint8, device="cuda:0")
+    outs = [buf[i * slot:i * slot + pb] for i in range(len(scales))]
+    say("quantize_rows_scales", M, K, dtype, G, scales)
+    cr.convrot_quantize_rows_scales(dev_x(X), G, scales, packed=outs)
+    got = host(buf)
+    for i, a in enumerate(scales):
+        want = orc.quantize_rows(X, G, a, threads=THREADS).raw
+        assert_bits_equal(got[i * slot:i * slot + pb], want, f"scale {a}")
+        assert np.all(got[i * slot + pb:(i + 1) * slot] == 0x5A), f"wrote past packed tensor {i}"
+
+
 # (rows, K, dtype, G): 131 073 bf16 rows of 256 make 2049 workgroups of 64
 # rows (8196 waves) with three pad rows and 60 rows past the packed tensor in
 # the last workgroup; 1025 binary32 rows of 32 768 take the workgroup kernel
