@@ -536,6 +536,11 @@ def main() -> int:
     if w.w_bits == 8 and not args.no_probe:
         rec["roofline"]["mfma_ceiling"] = mfma_ceiling(cr, torch, sets[0]["views"][0][0],
                                                        sets[0]["lins"][0]["Qw"], g_tops)
+    # the vendor library's int8 GEMM on the same operands, for reference: one
+    # linear's contraction alone (int32 output, no reconstruction), back to
+    # back over the same input sets
+    if w.w_bits == 8 and not w.swiglu and not args.no_probe and w.M > 16 and w.N % 8 == 0:
+        rec["roofline"]["library_gemm"] = library_gemm(torch, sets, w, args.steps, kernel_us)
     if shared:
         warm(step_folded)
         wall_f, _ = timed(step_folded, args.steps)
@@ -576,6 +581,25 @@ def probe_library():
                                            ctypes.c_void_p, ctypes.c_void_p]
         _PROBE = lib
     return _PROBE
+
+
+def library_gemm(torch, sets, w, steps: int, kernel_us) -> dict:
+    """torch._int_mm (hipBLASLt on ROCm) on the first linear's operands: Q_x
+    [M, K] times Q_w^T, int32 out.  Not part of the path: a reference for the
+    contraction alone."""
+    outs = [torch.empty((w.M, w.N), dtype=torch.int32, device=S["Y"][0].device) for S in sets]
+
+    def run(i):
+        S = sets[i % len(sets)]
+        torch._int_mm(S["views"][0][0][:w.M], S["lins"][0]["Qw"].t(), out=outs[i % len(sets)])
+    run(0)
+    torch.cuda.synchronize()
+    us = kernel_us(run)
+    ops = 2 * w.M * w.N * w.K
+    return {"what": "torch._int_mm (hipBLASLt) on the first linear's Q_x and Q_w: int32 output, no "
+                    "reconstruction, back to back",
+            "us": round(us, 3), "achieved": round(ops / us / 1e6, 1),
+            "frac": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
 
 
 def mfma_ceiling(cr, torch, qx, qw, gemm_tops: float) -> dict:
