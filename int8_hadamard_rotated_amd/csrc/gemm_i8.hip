@@ -458,6 +458,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     void *Yv = L.Y;
     const int64_t ldy = L.ldy;
     const float alpha = L.alpha;
+    // A divisor 2^k with 2^k and 2^-k both normal (exponent field 1 .. 253)
+    // has the exact reciprocal 2^-k, and x * 2^-k and x / 2^k are then the
+    // correct roundings of the same real number: such tiles multiply, one
+    // operation instead of the division's ten.  (alpha > 0 by contract.)
+    const uint32_t alpha_field = (__builtin_bit_cast(uint32_t, alpha) >> 23) & 0xFFu;
+    const bool alpha_pow2 = (__builtin_bit_cast(uint32_t, alpha) & 0x7FFFFFu) == 0u && alpha_field >= 1u &&
+                            alpha_field <= 253u;
+    const float alpha_inv = __builtin_bit_cast(float, (254u - alpha_field) << 23);
     const int row_in = 4 * (lane >> 4), col_in = lane & 15;
     const int cq = lane % kColQuads, rr0 = lane / kColQuads;
     const int cl = wn * T::kWaveN + 4 * cq;                     // column within the tile
@@ -638,12 +646,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     for (int e = 0; e < 4; ++e) {
                         float x = (float)a[e];
                         x = x * sxr;
-                        x = x * sw[e];
-                        if constexpr (TDIV)
-                            x = __fdiv_rn(x, alpha);
-                        x = x + bo[e];
-                        t[e] = x;
+                        t[e] = x * sw[e];
                     }
+                    if constexpr (TDIV) {
+                        // uniform per tile: a power-of-two divisor multiplies
+                        // by its exact reciprocal (same bits, see alpha_inv)
+                        if (alpha_pow2) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                t[e] = t[e] * alpha_inv;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                t[e] = __fdiv_rn(t[e], alpha);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        t[e] = t[e] + bo[e];
                     if constexpr (POST) {
                         if (has_post) {
                             // fl(fl(fl(y * scale) * gate) + residual), the residual in

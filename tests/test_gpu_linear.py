@@ -109,14 +109,16 @@ def test_int8_linear_bit_exact(orc, y_dtype, M, K, N):
 BIG_GRID = (2051, 512, 5125)
 
 
+@pytest.mark.parametrize("alpha", [0.3, 0.5, 2.0 ** -20])
 @pytest.mark.parametrize("y_dtype", [oracle.F32, oracle.BF16])
-def test_int8_linear_big_grid_unscale(orc, y_dtype):
+def test_int8_linear_big_grid_unscale(orc, y_dtype, alpha):
+    """The 256 x 256 kernels with the unscale: a correctly rounded division
+    for 0.3, a multiplication by the exact reciprocal for the powers of two."""
     M, K, N = BIG_GRID
     rng = np.random.default_rng(91 + y_dtype)
     X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
     W, b = workloads.gaussian_weights(rng, N, K)
     Qw, sw = orc.weight_prep(W, 256, threads=THREADS)
-    alpha = 0.3
     p = orc.quantize_rows(X, 256, alpha, threads=THREADS)
     A = orc.gemm_i32(p.q, Qw, threads=THREADS)
     want = orc.epilogue(A, p.s, sw, b, alpha, y_dtype, threads=THREADS)
@@ -161,13 +163,14 @@ def test_int8_linear_grouped(orc, M, K, Ns):
 @pytest.mark.parametrize("M,K,Ns", [(515, 768, (130, 64, 257)), (1030, 512, (3072, 3072, 3072))])
 def test_int8_linear_grouped_own_inputs(orc, M, K, Ns):
     """Linears of one launch reading different packed tensors: the pages'
-    path for two input scales (a quantization pass per scale, the division by
-    it in the reconstruction).  The second shape is 180 tiles of 256 x 256:
-    the kernel with the division compiled in, which its alpha = 1 tiles skip."""
+    path for several input scales (a quantization pass per scale, the
+    division by it in the reconstruction).  The second shape is 180 tiles of
+    256 x 256: the kernel with the division compiled in, which its alpha = 1
+    tiles skip and its alpha = 0.5 tiles replace by the exact reciprocal."""
     rng = np.random.default_rng(M + 7 * K)
     G = 256
     X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
-    alphas = (1.0, 0.3, 1.0)
+    alphas = (1.0, 0.3, 0.5)
     packs = {a: orc.quantize_rows(X, G, a, threads=THREADS) for a in set(alphas)}
     dpacks = {a: (dev(p.q), dev(p.s)) for a, p in packs.items()}
     lins, wants = [], []
