@@ -480,7 +480,7 @@ constexpr int kParamLdsBytes = 48 * 1024;
 // direct path; it only changes where the values wait.
 // RMSNorm with Modulate's scale and shift staged in LDS, at alpha = 1: capped
 // for three waves per SIMD (168 registers), so that a pass of three waves per
-// SIMD runs in one round (4096 x 3072 bf16: 20.35 -> 19.32 us on one box).
+// SIMD runs in one round (4096 x 3072 bf16: 20.35 -> 19.32 us, A/B on MI355X).
 // The other RMSNorm kernels keep two: the cap spills registers there.
 template <bool SCALED, int MOD, bool RMS, bool PS>
 constexpr int kQuantizeWaves = (RMS && PS && MOD == 2 && !SCALED) ? 3 : 1;
@@ -970,7 +970,7 @@ hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float 
     if (sizeof(XT) == 2 && stage_vec && !RMS) {
         // every workgroup copies the vectors once: workgroups of up to 1024
         // threads share the copy among more rows (4096 x 3072 bf16 with
-        // scale and shift: 16 rows, 13.56 -> 12.87 us on one box; RMSNorm's
+        // scale and shift: 16 rows, 13.56 -> 12.87 us in an A/B run; RMSNorm's
         // 512-thread kernels gained nothing from more rows)
         while (4 * qr * rows * 2 <= kMaxThreads)
             rows *= 2;
@@ -1034,8 +1034,8 @@ hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float 
     }
     if constexpr (ACT == 0 && MOD == 0 && !RMS) {
         // Plain rows with direct code stores (passes of few wave rounds) run
-        // the rotation's split digits four in lockstep: identical bytes, on
-        // one box 4096 x 3072 bf16 10.45 -> 10.04 us.  Passes of many rounds
+        // the rotation's split digits four in lockstep: identical bytes, in
+        // an A/B run 4096 x 3072 bf16 10.45 -> 10.04 us.  Passes of many rounds
         // (the wave-store path) keep the plain order: there the lockstep form
         // measured 105.5 -> 110.1 us on 16384 x 12288 bf16.
         if (!wave_store)
