@@ -118,15 +118,19 @@ __device__ __forceinline__ void load8(const float *src, float (&v)[8])
 }
 
 // bf16 -> binary32 is exact: the bf16 bits are the upper half.
-__device__ __forceinline__ void load8(const uint16_t *src, float (&v)[8])
+__device__ __forceinline__ void widen8(const v4u &u, float (&v)[8])
 {
-    const v4u u = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src));
     const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
         v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
     }
+}
+
+__device__ __forceinline__ void load8(const uint16_t *src, float (&v)[8])
+{
+    widen8(__builtin_nontemporal_load(reinterpret_cast<const v4u *>(src)), v);
 }
 
 // Four independent H4s of split digits (each as h4_split) in lockstep: every
@@ -555,21 +559,64 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024, (kQuantizeWaves<SCA
         const int n_threads = (int)blockDim.x;
         const int row_len = (int)K;
         const int elems = rows_per_wg * row_len;
+        if constexpr (sizeof(XT) == 2) {
+            // bf16: the next piece's raw 16-byte loads are issued before this
+            // piece's activation, so that their latency runs under it
+            // (4096 x 12288: 124.8 -> 118.9 us in an A/B run; binary32 rows,
+            // twice the raw registers, ran 5% slower this way)
+            const int stride = 8 * n_threads;
+            // Every lane loads every round; a piece past the rows reads row
+            // M - 1 instead (in bounds, not used), so that no loaded register
+            // is merged with another value before it is needed.
+            auto fetch = [&](int ee, v4u &rg, v4u &ru) -> bool {
+                const int rl = ee / row_len;
+                const int64_t grow = (int64_t)blockIdx.x * rows_per_wg + rl;
+                const bool valid = ee < elems && grow < M;
+                const int64_t r = valid ? grow : M - 1;
+                const int col = valid ? ee - rl * row_len : 0;
+                rg = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(X + r * ldx + col));
+                ru = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(up + r * ld_up + col));
+                return valid;
+            };
+            int e = 8 * tid;
+            v4u rg, ru;
+            bool ok = fetch(e, rg, ru);
 #pragma unroll 1
-        for (int e = 8 * tid; e < elems; e += 8 * n_threads) {   // element of the rows laid end to end
-            const int rl = e / row_len;
-            const int col = e - rl * row_len;
-            const int64_t grow = (int64_t)blockIdx.x * rows_per_wg + rl;
-            if (grow < M) {
-                float g[8], u[8];
-                load8(X + grow * ldx + col, g);
-                load8(up + grow * ld_up + col, u);
+            for (; e < elems; e += stride) {
+                v4u ng, nu;
+                const bool okn = fetch(e + stride, ng, nu);
+                if (ok) {
+                    float g[8], u[8];
+                    widen8(rg, g);
+                    widen8(ru, u);
 #pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    g[p] = gated_act<ACT>(g[p]) * u[p];
-                float *dst = act_stage + act_index(e);
-                *reinterpret_cast<v4f *>(dst) = v4f{g[0], g[1], g[2], g[3]};
-                *reinterpret_cast<v4f *>(dst + 4) = v4f{g[4], g[5], g[6], g[7]};
+                    for (int p = 0; p < 8; ++p)
+                        g[p] = gated_act<ACT>(g[p]) * u[p];
+                    float *dst = act_stage + act_index(e);
+                    *reinterpret_cast<v4f *>(dst) = v4f{g[0], g[1], g[2], g[3]};
+                    *reinterpret_cast<v4f *>(dst + 4) = v4f{g[4], g[5], g[6], g[7]};
+                }
+                rg = ng;
+                ru = nu;
+                ok = okn;
+            }
+        } else {
+#pragma unroll 1
+            for (int e = 8 * tid; e < elems; e += 8 * n_threads) {   // element of the rows laid end to end
+                const int rl = e / row_len;
+                const int col = e - rl * row_len;
+                const int64_t grow = (int64_t)blockIdx.x * rows_per_wg + rl;
+                if (grow < M) {
+                    float g[8], u[8];
+                    load8(X + grow * ldx + col, g);
+                    load8(up + grow * ld_up + col, u);
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        g[p] = gated_act<ACT>(g[p]) * u[p];
+                    float *dst = act_stage + act_index(e);
+                    *reinterpret_cast<v4f *>(dst) = v4f{g[0], g[1], g[2], g[3]};
+                    *reinterpret_cast<v4f *>(dst + 4) = v4f{g[4], g[5], g[6], g[7]};
+                }
             }
         }
         __syncthreads();
