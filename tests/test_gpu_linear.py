@@ -190,6 +190,77 @@ def test_int8_linear_grouped_own_inputs(orc, M, K, Ns):
         assert_bits_equal(host(y), want, f"grouped linear {j} alpha={alphas[j]}")
 
 
+GROUPED_SIXTEEN = [(300, 256, (0, 1, 17, 64, 130, 256, 257, 3, 0, 96, 33, 512, 5, 128, 200, 64)),
+                   (1030, 256, (520, 600, 257, 512, 700, 1, 513, 640, 300, 768, 129, 512, 64, 900, 256,
+                                500))]
+
+
+@pytest.mark.parametrize("M,K,Ns", GROUPED_SIXTEEN)
+def test_int8_linear_grouped_sixteen(orc, M, K, Ns):
+    """Sixteen linears in one launch (the most it takes): empty, one-column
+    and ragged outputs, both output dtypes, five input scales.  Even linears
+    read the call's packed tensor (alpha = 1), odd ones their own.  The
+    first shape runs 128 x 128 tiles; the second is 180 tiles of 256 x 256
+    with the division compiled in."""
+    rng = np.random.default_rng(M + 3 * K)
+    G = 256
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16)
+    own = (0.3, 0.5, 2.0, 0.7)
+    packs = {a: orc.quantize_rows(X, G, a, threads=THREADS) for a in (1.0, *own)}
+    dpacks = {a: (dev(p.q), dev(p.s)) for a, p in packs.items()}
+    lins, wants = [], []
+    for j, N in enumerate(Ns):
+        a = 1.0 if j % 2 == 0 else own[(j // 2) % len(own)]
+        yd = oracle.BF16 if j % 3 == 0 else oracle.F32
+        if N == 0:
+            Qw, sw = np.zeros((0, K), np.int8), np.zeros(0, np.float32)
+            b = np.zeros(0, np.float32)
+            wants.append(None)
+        else:
+            W, b = workloads.gaussian_weights(rng, N, K)
+            Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+            A = orc.gemm_i32(packs[a].q, Qw, threads=THREADS)
+            wants.append(orc.epilogue(A, packs[a].s, sw, b, a, yd, threads=THREADS))
+        lin = dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=yd)
+        if j % 2 == 1:
+            lin["Qx"], lin["s_x"] = dpacks[a]
+        lins.append(lin)
+    say("int8_linear_grouped sixteen", M, K, Ns)
+    qx, sx = dpacks[1.0]
+    outs = cr.int8_linear_grouped(qx, sx, lins)
+    for j, (y, want) in enumerate(zip(outs, wants)):
+        if want is None:
+            assert tuple(y.shape) == (M, 0)
+            continue
+        check_y(host(y), want, lins[j]["y_dtype"], f"grouped linear {j} N={Ns[j]}")
+
+
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.BF16])
+def test_shared_sixteen_scales(orc, dtype):
+    """convrot_int8_linear_shared with sixteen linears of sixteen distinct
+    input scales: sixteen packed tensors in the workspace (binary32 rows two
+    scales per pass, bf16 rows one), then one grouped launch over all of
+    them, against the oracle's literal path."""
+    import torch
+    rng = np.random.default_rng(99 + (dtype == workloads.BF16))
+    M, K, G = 130, 512, 64
+    X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, dtype)
+    scales = [0.3, 0.7, 1.0, 1.3, 0.11, 3.7, 0.9, 1.1, 0.6, 2.5, 0.45, 6.0, 0.35, 1.7, 0.15, 4.2]
+    Ns = [64, 17, 130, 1, 96, 256, 33, 128, 5, 64, 200, 48, 3, 160, 80, 32]
+    preps, lins = [], []
+    for a, N in zip(scales, Ns):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        preps.append((Qw, sw, b))
+        lins.append(dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a, y_dtype=oracle.F32))
+    ws = torch.empty(cr.convrot_workspace_bytes(M, K, len(scales)), dtype=torch.uint8, device="cuda:0")
+    say("shared sixteen scales", dtype)
+    outs = [host(y) for y in cr.convrot_int8_linear_shared(dev_x(X), G, lins, workspace=ws)]
+    for (Qw, sw, b), a, y in zip(preps, scales, outs):
+        want = orc.linear(X, G, Qw, sw, b, a, oracle.F32, threads=THREADS)
+        check_y(y, want, oracle.F32, f"alpha={a}")
+
+
 def test_shared_mixed_scales_big_grid(orc):
     """convrot_int8_linear_shared with alpha = 1 and alpha = 0.3 linears: two
     quantization passes, then one grouped launch of 180 tiles of 256 x 256

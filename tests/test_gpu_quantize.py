@@ -71,7 +71,12 @@ SCALES_CASES = [(4096, 3072, workloads.F32, 256, (1.0, 0.5)),
                 (17, 192, workloads.F32, 4, (3.0, 1.0)),
                 (6, 8192, workloads.F32, 256, (1.0, 0.3)),
                 (3, 32768, workloads.F32, 256, (1.0, 0.3)),
-                (129, 3072, workloads.BF16, 256, (1.0, 0.5, 0.3))]
+                (129, 3072, workloads.BF16, 256, (1.0, 0.5, 0.3)),
+                # sixteen scales (the most a call takes): eight two-scale passes
+                (77, 1024, workloads.F32, 256, (1.0, 0.3, 0.5, 0.7, 1.3, 2.0, 0.11, 3.7, 0.25, 5.0, 0.9,
+                                                1.1, 0.6, 2.5, 0.45, 8.0)),
+                (50, 768, workloads.BF16, 64, (0.3, 0.7, 1.0, 1.9, 0.5)),
+                (5, 4096, workloads.F32, 16, (0.3, 0.7, 1.0))]
 
 
 @pytest.mark.parametrize("M,K,dtype,G,scales", SCALES_CASES)
