@@ -101,6 +101,7 @@ class Oracle:
             "oracle_quantize_rows": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i32]),
             "oracle_modulate_rows": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32]),
             "oracle_rmsnorm_rows": (i32, [vp, i32, i64, i64, i64, f32, vp, vp, i32]),
+            "oracle_norm_rows": (i32, [vp, i32, i64, i64, i64, f32, vp, vp, i32]),
             "oracle_expf": (f32, [f32]),
             "oracle_expf_array": (i32, [vp, vp, i64, i32]),
             "oracle_gated_act_rows": (i32, [vp, i32, i64, i64, i64, vp, i64, i32, vp, i32]),
@@ -182,6 +183,22 @@ class Oracle:
         rc = self.lib.oracle_rmsnorm_rows(_p(X), code, M, K, ldx, ctypes.c_float(eps),
                                           None if w is None else _p(w), _p(Y), threads)
         self._check(rc, "rmsnorm_rows")
+        return Y
+
+    def norm_rows(self, X: np.ndarray, eps: float, weight=None, K: int | None = None,
+                  threads: int = 1) -> np.ndarray:
+        """Norm (mean and variance) -> Mul(weight) on the first K columns of X:
+        binary32 [M, K]."""
+        code = _dtype_code(X)
+        X = np.ascontiguousarray(X)
+        M, ldx = X.shape
+        K = ldx if K is None else K
+        w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float32)
+        assert w is None or w.shape == (K,)
+        Y = np.empty((M, K), dtype=np.float32)
+        rc = self.lib.oracle_norm_rows(_p(X), code, M, K, ldx, ctypes.c_float(eps),
+                                       None if w is None else _p(w), _p(Y), threads)
+        self._check(rc, "norm_rows")
         return Y
 
     def expf(self, x: float) -> float:

@@ -55,6 +55,16 @@
  *     those sums, ...) and the K/64 block sums are added left to right; then
  *     mean = fl(S / K), d = fl(sqrt(fl(mean + eps))), r = fl(1 / d) (each
  *     correctly rounded), y = fl(x * r) and, with a weight, fl(y * w[i]).
+ *   - Norm -> Mul(weight) ahead of the quantizer (same page and section, the
+ *     Norm -> Mul -> ConvRot fusion; the page names the chain only): Norm is
+ *     the normalization by mean and variance with no affine part, and Mul
+ *     multiplies by a weight vector of length K shared by every row, as in
+ *     the RMSNorm chain.  Per row, the features x are summed in the tree
+ *     above (pairwise within 64-feature blocks, block sums left to right),
+ *     mean = fl(S1 / K); then the deviations d = fl(x - mean) give
+ *     fl(d * d), summed in the same tree, var = fl(S2 / K),
+ *     r = fl(1 / fl(sqrt(fl(var + eps)))) (correctly rounded), y = fl(d * r)
+ *     and, with a weight, fl(y * w[i]).
  *   - the gated activation ahead of the quantizer (same page and section:
  *     SiLU/Sigmoid -> Mul -> ConvRot, and SwiGLU -> ConvRot with its gate and
  *     up halves): z = fl(act(g) * u) with g the quantizer's input and u a
@@ -343,6 +353,55 @@ int oracle_rmsnorm_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_
         const float rs = 1.0f / d;
         for (int64_t i = 0; i < K; ++i) {
             float y = load_widened(X, x_dtype, r * ldx + i) * rs;
+            if (weight)
+                y = y * weight[i];
+            Y[r * K + i] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Norm -> Mul(weight) (page "ggml operator extensions", section "sd.cpp
+ * integration", the Norm -> Mul -> ConvRot fusion), in the reading stated at
+ * the top of this file: the row mean, then the mean of the squared
+ * deviations, both summed in RMSNorm's tree.  weight may be NULL (no
+ * multiplication).  K must be a multiple of 64.  Y is binary32 [M][K],
+ * contiguous.
+ */
+int oracle_norm_rows(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, float eps,
+                     const float *weight, float *Y, int threads)
+{
+    if (!X || !Y || M < 0 || K < 64 || K % 64 != 0 || ldx < K || !(eps >= 0.0f) || isinf(eps))
+        return ORACLE_EINVAL;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_EUNSUPPORTED;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t r = 0; r < M; ++r) {
+        float t[64];
+        float S1 = 0.0f;
+        for (int64_t b = 0; b < K; b += 64) {
+            for (int i = 0; i < 64; ++i)
+                t[i] = load_widened(X, x_dtype, r * ldx + b + i);
+            const float block = pairwise_sum64(t);
+            S1 = b == 0 ? block : S1 + block;
+        }
+        const float mean = S1 / (float)K;
+        float S2 = 0.0f;
+        for (int64_t b = 0; b < K; b += 64) {
+            for (int i = 0; i < 64; ++i) {
+                const float dv = load_widened(X, x_dtype, r * ldx + b + i) - mean;
+                t[i] = dv * dv;
+            }
+            const float block = pairwise_sum64(t);
+            S2 = b == 0 ? block : S2 + block;
+        }
+        const float var = S2 / (float)K;
+        const float sd = sqrtf(var + eps);
+        const float rs = 1.0f / sd;
+        for (int64_t i = 0; i < K; ++i) {
+            const float dv = load_widened(X, x_dtype, r * ldx + i) - mean;
+            float y = dv * rs;
             if (weight)
                 y = y * weight[i];
             Y[r * K + i] = y;

@@ -526,6 +526,117 @@ def pin_rmsnorm_fp64_bound(o):
             assert np.all(np.abs(got - ref) <= bound), f"K={K} eps={eps}: {np.max(np.abs(got - ref) / bound)}"
 
 
+def tree_sum_f32(vals: list) -> Fraction:
+    """The reading's sum order in exact rationals rounded to binary32 after
+    every addition: pairwise inside each block of 64 (adjacent pairs first),
+    then the block sums left to right."""
+    S = None
+    for b in range(0, len(vals), 64):
+        t = list(vals[b:b + 64])
+        while len(t) > 1:
+            t = [rne_f32(t[2 * i] + t[2 * i + 1]) for i in range(len(t) // 2)]
+        S = t[0] if S is None else rne_f32(S + t[0])
+    return S
+
+
+def norm_exact(xw: np.ndarray, eps: float, w) -> list:
+    """One row of Norm -> Mul(weight) in exact rationals with binary32 rounding
+    after every operation: the mean, the deviations, the mean of their
+    squares, the correctly rounded root and reciprocal, then the products."""
+    K = len(xw)
+    mean = rne_f32(tree_sum_f32([F(x) for x in xw]) / K)
+    d = [rne_f32(F(x) - mean) for x in xw]
+    var = rne_f32(tree_sum_f32([rne_f32(v * v) for v in d]) / K)
+    r = rne_f32(1 / sqrt_rn_f32(rne_f32(var + F(np.float32(eps)))))
+    out = []
+    for i, v in enumerate(d):
+        y = rne_f32(v * r)
+        if w is not None:
+            y = rne_f32(y * F(w[i]))
+        out.append(y)
+    return out
+
+
+def pin_norm_exact(o):
+    """Norm -> Mul(weight) against exact rational arithmetic with binary32
+    rounding (and a correctly rounded square root) at each step, for binary32
+    and bf16 rows with a non-zero mean, with and without the weight (page
+    "ggml operator extensions", the Norm -> Mul -> ConvRot fusion)."""
+    rng = np.random.default_rng(146)
+    M, K = 2, 192
+    X = (workloads.gaussian_activations(rng, M, K, 0.05, 20.0, workloads.F32) +
+         np.float32(2.5)).astype(np.float32)
+    w = (1.0 + rng.standard_normal(K) * 0.2).astype(np.float32)
+    Xb = workloads.f32_to_bf16_bits(X)
+    for src, xw in ((X, X), (Xb, workloads.bf16_bits_to_f32(Xb))):
+        for weight in (w, None):
+            for eps in (1e-6, 0.5):
+                Y = o.norm_rows(src, eps, weight)
+                for r in range(M):
+                    want = norm_exact(xw[r], eps, weight)
+                    for i in range(K):
+                        assert F_out(Y[r, i]) == want[i], f"norm ({r},{i}) eps={eps} w={weight is not None}"
+
+
+def pin_norm_closed_forms(o):
+    """Rows alternating c + a and c - a (c, a powers of two or zero, every sum
+    exact) normalize to +-1 exactly with eps = 0, times the weight with one;
+    constant rows and zero rows give zeros for eps > 0; with eps = 0 scaling a
+    row by 2^k changes nothing; rows whose adjacent pairs are (v, -v) have
+    mean 0 exactly and equal the RMSNorm chain bit for bit; a row stride is
+    honoured."""
+    K = 256
+    sign = np.tile(np.array([1.0, -1.0], np.float32), K // 2)
+    rows = [np.float32(c) + np.float32(a) * sign for c in (0.0, 3.0, -96.0, 2.0 ** 20)
+            for a in (2.0 ** -3, 1.0, 2.0 ** 7)]
+    X = np.stack(rows).astype(np.float32)
+    assert np.all(np.abs(np.abs(X - X.mean(axis=1, keepdims=True)) - np.abs(X[:, :1] - X[:, 1:2]) / 2) == 0)
+    assert np.array_equal(o.norm_rows(X, 0.0), np.broadcast_to(sign, X.shape)), "c +- a rows"
+    rng = np.random.default_rng(147)
+    w = rng.standard_normal(K).astype(np.float32)
+    assert np.array_equal(o.norm_rows(X, 0.0, w), np.broadcast_to(sign * w, X.shape)), "c +- a rows, weight"
+    C = np.stack([np.full(K, c, np.float32) for c in (0.0, 1.0, -7.5, 2.0 ** 40)])
+    assert np.array_equal(o.norm_rows(C, 1e-5, w), np.zeros((4, K))), "constant rows"
+    R = workloads.gaussian_activations(rng, 4, K, 0.01, 20.0, workloads.F32) + np.float32(1.5)
+    base = o.norm_rows(R, 0.0, w)
+    for k in (-9, 5, 21):
+        assert np.array_equal(o.norm_rows((R * 2.0 ** k).astype(np.float32), 0.0, w), base), f"2^{k}"
+    P = workloads.gaussian_activations(rng, 3, K, 0.01, 20.0, workloads.F32)
+    P[:, 1::2] = -P[:, 0::2]
+    for eps in (0.0, 1e-6, 0.5):
+        assert np.array_equal(o.norm_rows(P, eps, w), o.rmsnorm_rows(P, eps, w)), f"zero-mean rows eps={eps}"
+    wide = workloads.gaussian_activations(rng, 3, K + 64, 0.01, 20.0, workloads.F32)
+    assert np.array_equal(o.norm_rows(wide, 1e-6, w, K=K),
+                          o.norm_rows(np.ascontiguousarray(wide[:, :K]), 1e-6, w))
+
+
+def pin_norm_fp64_bound(o):
+    """Against (x - mean(x)) / sqrt(var(x) + eps) * w in binary64, for rows
+    with means from 0 to several deviations, eps well below and well above
+    the variance.  The binary32 steps err by at most (8 + K/64) units in the
+    mean (in units of the mean absolute value) and in the variance; the bound
+    adds the mean's error, carried by every deviation, to a relative error
+    of the same order on each output."""
+    rng = np.random.default_rng(148)
+    for K in (64, 1024, 3072):
+        for shift in (0.0, 4.0):
+            X = (workloads.gaussian_activations(rng, 3, K, 0.005, 30.0, workloads.F32) +
+                 np.float32(shift)).astype(np.float32)
+            w = (1.0 + rng.standard_normal(K) * 0.2).astype(np.float32)
+            x64 = X.astype(np.float64)
+            mu = x64.mean(axis=1, keepdims=True)
+            var = ((x64 - mu) ** 2).mean(axis=1, keepdims=True)
+            for eps in (1e-6, 4.0 * float(var.mean())):
+                sd = np.sqrt(var + float(np.float32(eps)))
+                ref = (x64 - mu) / sd * w
+                got = o.norm_rows(X, eps, w).astype(np.float64)
+                g = 8 + K / 64
+                mean_abs = np.abs(x64).mean(axis=1, keepdims=True)
+                bound = (2 * g * U32 * mean_abs / sd * np.abs(w) + (g / 2 + 8) * U32 * np.abs(ref) + 1e-30)
+                assert np.all(np.abs(got - ref) <= bound), \
+                    f"K={K} shift={shift} eps={eps}: {np.max(np.abs(got - ref) / bound)}"
+
+
 def exp_exact_f32(x: float) -> Fraction:
     """exp(x) to 60 significant digits (Python's decimal), then rounded to
     binary32 by the IEEE rule above: the correctly rounded binary32 exp."""

@@ -69,6 +69,17 @@ MUTATIONS = {
     "rms_abs_not_square": ("sq[i] = x * x;", "sq[i] = fabsf(x);"),
     "rms_weight_reversed": ("y = y * weight[i];", "y = y * weight[K - 1 - i];"),
     "rms_last_block_only": ("S = b == 0 ? block : S + block;", "S = block;"),
+    "norm_var_uncentered": ("const float dv = load_widened(X, x_dtype, r * ldx + b + i) - mean;",
+                            "const float dv = load_widened(X, x_dtype, r * ldx + b + i);"),
+    "norm_output_uncentered": ("const float dv = load_widened(X, x_dtype, r * ldx + i) - mean;",
+                               "const float dv = load_widened(X, x_dtype, r * ldx + i);"),
+    "norm_var_sum_not_mean": ("const float var = S2 / (float)K;", "const float var = S2;"),
+    "norm_mean_over_blocks": ("const float mean = S1 / (float)K;", "const float mean = S1 / (float)(K / 64);"),
+    "norm_eps_after_root": ("const float sd = sqrtf(var + eps);", "const float sd = sqrtf(var) + eps;"),
+    "norm_no_reciprocal": ("const float rs = 1.0f / sd;", "const float rs = sd;"),
+    "norm_weight_reversed": ("float y = dv * rs;\n            if (weight)\n                y = y * weight[i];",
+                             "float y = dv * rs;\n            if (weight)\n                y = y * weight[K - 1 - i];"),
+    "norm_last_block_only": ("S2 = b == 0 ? block : S2 + block;", "S2 = block;"),
     "act_exp_sign": ("const float e = oracle_expf(-g);", "const float e = oracle_expf(g);"),
     "act_no_one": ("const float d = 1.0f + e;", "const float d = e;"),
     "act_silu_is_sigmoid": ("const float a = act == ORACLE_ACT_SILU ? g * sg : sg;", "const float a = sg;"),
