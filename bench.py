@@ -61,11 +61,11 @@ def source_hash(path: str) -> str:
 def quantize_bytes(w: workloads.Workload, n_scales: int = 1) -> int:
     """Algorithmic bytes of the quantization of one step: read X once (and
     the producer's inputs, if any: the gated activation's second tensor, the
-    RMSNorm weight, the Modulate scale and shift), write the packed tensor of
+    normalization weight, the Modulate scale and shift), write the packed tensor of
     each of the n_scales input scales."""
     esz = 2 if w.x_dtype == workloads.BF16 else 4
     m_pad = (w.M + 3) // 4 * 4
-    mod = (8 * w.K if w.modulate else 0) + (4 * w.K if w.rmsnorm else 0)
+    mod = (8 * w.K if w.modulate else 0) + (4 * w.K if w.rmsnorm or w.norm else 0)
     up = w.M * w.K * esz if w.glu else 0
     return w.M * w.K * esz + up + n_scales * (m_pad * w.K + 4 * m_pad) + mod
 
@@ -198,6 +198,8 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
         X = o.gated_act_rows(X, np.ascontiguousarray(inp.up[:rows]), w.glu, threads=threads)
     if w.rmsnorm:
         X = o.rmsnorm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
+    if w.norm:
+        X = o.norm_rows(X, w.rms_eps, inp.norm_weight, threads=threads)
     if w.modulate:
         X = o.modulate_rows(X, inp.mod_scale, inp.mod_shift, threads=threads)
     t1 = time.perf_counter()
@@ -226,6 +228,7 @@ def cpu_baseline(w: workloads.Workload, inp: workloads.Inputs, rows: int) -> dic
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {w.M} rows of {w.name} ({'gated activation + ' if w.glu else ''}"
                       f"{'RMSNorm + ' if w.rmsnorm else ''}"
+                      f"{'Norm + ' if w.norm else ''}"
                       f"{'modulate + ' if w.modulate else ''}"
                       f"quantize + int32 GEMM + reconstruction{' + gated residual' if w.gated else ''}"
                       f"{' for the gate and up weights + SwiGLU' if w.swiglu else ''} "
@@ -346,6 +349,8 @@ def main() -> int:
     if w.rmsnorm:
         mod = cr.RMSNormModulate(w.rms_eps, torch.from_numpy(inp.norm_weight).to(dev),
                                  mod.scale if mod else None, mod.shift if mod else None)
+    if w.norm:
+        mod = cr.NormMul(w.rms_eps, torch.from_numpy(inp.norm_weight).to(dev))
     gate = torch.from_numpy(inp.gate).to(dev) if w.gated else None
     slot = cr.convrot_workspace_bytes(w.M, w.K, 1)
 
@@ -470,6 +475,7 @@ def main() -> int:
                                + (", SiLU(X) * up fused" if w.glu == 1 else ", Sigmoid(X) * up fused" if w.glu else "")
                                + (", one dual GEMM with the SwiGLU epilogue (gate, up)" if w.swiglu else "")
                                + (", RMSNorm -> Mul(weight) fused" if w.rmsnorm else "")
+                               + (", Norm -> Mul(weight) fused" if w.norm else "")
                                + (", Modulate producer fused" if w.modulate else "")
                                + (", gated residual in place" if w.gated else ""),
                    "M": w.M, "K": w.K, "N": w.N, "G": w.G, "x_dtype": w.x_dtype,

@@ -256,6 +256,19 @@ int convrot_int8_linear_shared(const void *X, int x_dtype, int64_t M, int64_t K,
  * Rows are limited to half the quantizer's K (32768 when K % 256 == 0), else
  * CONVROT_EUNSUPPORTED.
  *
+ * CONVROT_PRE_NORM_MUL (same page and section: the Norm -> Mul -> ConvRot
+ * fusion; the page names the chain only): Norm divides the deviations from
+ * the row mean by the root of the row variance plus eps, with no affine part,
+ * and Mul multiplies by the per-channel norm_weight when given.  Per row,
+ * with x the widened input and sums taken in RMSNorm's order above:
+ *     mean = fl(S1 / K),  S1 = sum of x
+ *     d    = fl(x - mean)
+ *     r    = fl(1 / fl(sqrt(fl(fl(S2 / K) + eps)))),  S2 = sum of fl(d * d)
+ *     x'   = fl(d * r), then fl(x' * norm_weight[i]) when norm_weight is given
+ * scale and shift must be NULL (no Modulate in this chain); eps and the row
+ * limit as for RMSNORM_MODULATE.  A row whose values are all equal has d = 0
+ * and gives zeros for eps > 0 (NaN for eps = 0, outside the contract).
+ *
  * CONVROT_PRE_GATED_ACT (same page and section: SiLU/Sigmoid -> Mul ->
  * ConvRot, and SwiGLU -> ConvRot with packed, swapped or separate gate/up
  * inputs): with g the quantizer's input X and u = up[r][i], a second tensor
@@ -272,7 +285,8 @@ typedef enum {
     CONVROT_PRE_NONE = 0,
     CONVROT_PRE_MODULATE = 1,
     CONVROT_PRE_RMSNORM_MODULATE = 2,
-    CONVROT_PRE_GATED_ACT = 3
+    CONVROT_PRE_GATED_ACT = 3,
+    CONVROT_PRE_NORM_MUL = 4
 } convrot_pre_kind;
 
 typedef enum { CONVROT_ACT_SILU = 1, CONVROT_ACT_SIGMOID = 2 } convrot_act;
@@ -281,8 +295,8 @@ typedef struct {
     int kind;                  /* convrot_pre_kind */
     const float *scale;        /* MODULATE: [K] (device), required; RMSNORM_MODULATE: [K] or NULL */
     const float *shift;        /* [K] (device) or NULL */
-    const float *norm_weight;  /* RMSNORM_MODULATE: [K] (device) or NULL */
-    float eps;                 /* RMSNORM_MODULATE: added to the mean square */
+    const float *norm_weight;  /* RMSNORM_MODULATE, NORM_MUL: [K] (device) or NULL */
+    float eps;                 /* RMSNORM_MODULATE: added to the mean square; NORM_MUL: to the variance */
     const void *up;            /* GATED_ACT: [M][ld_up] (device), X's dtype */
     int64_t ld_up;             /* GATED_ACT: elements, >= K */
     int act;                   /* GATED_ACT: convrot_act */
@@ -290,8 +304,9 @@ typedef struct {
 
 /* convrot_quantize_rows with a producer.  pre may be NULL or of kind
  * CONVROT_PRE_NONE (then identical to convrot_quantize_rows).  CONVROT_EINVAL
- * for a MODULATE descriptor without scale, a shift without scale, a negative
- * or non-finite eps, or misaligned vectors (16 bytes); CONVROT_EUNSUPPORTED
+ * for a MODULATE descriptor without scale, a shift without scale, a
+ * NORM_MUL descriptor with scale or shift, a negative or non-finite eps, or
+ * misaligned vectors (16 bytes); CONVROT_EUNSUPPORTED
  * for an unknown kind; CONVROT_EOVERLAP if packed overlaps X or a vector. */
 int convrot_quantize_rows_pre(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                               const convrot_pre *pre, int group_size, float input_scale,

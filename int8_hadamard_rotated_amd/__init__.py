@@ -16,7 +16,7 @@ LIBRARY = os.path.join(_HERE, "libconvrot.so")
 
 OK, EINVAL, EUNSUPPORTED, EOVERFLOW, EOVERLAP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
-PRE_NONE, PRE_MODULATE, PRE_RMSNORM_MODULATE, PRE_GATED_ACT = 0, 1, 2, 3
+PRE_NONE, PRE_MODULATE, PRE_RMSNORM_MODULATE, PRE_GATED_ACT, PRE_NORM_MUL = 0, 1, 2, 3, 4
 ACT_SILU, ACT_SIGMOID = 1, 2
 POST_NONE, POST_GATED_RESIDUAL = 0, 1
 MAX_LINEARS = 16
@@ -85,6 +85,19 @@ class RMSNormModulate:
     def desc(self) -> PreDesc:
         ptr = lambda t: None if t is None else t.data_ptr()
         return PreDesc(PRE_RMSNORM_MODULATE, ptr(self.scale), ptr(self.shift), ptr(self.weight),
+                       self.eps)
+
+
+class NormMul:
+    """Norm (mean and variance) -> Mul(weight) ahead of the quantizer: eps, and
+    an optional float32 device weight of K elements (None: no multiplication)."""
+
+    def __init__(self, eps: float, weight=None):
+        self.eps = float(eps)
+        self.weight = weight
+
+    def desc(self) -> PreDesc:
+        return PreDesc(PRE_NORM_MUL, None, None, None if self.weight is None else self.weight.data_ptr(),
                        self.eps)
 
 

@@ -203,6 +203,23 @@ int check_gated_act(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, P
     return CONVROT_OK;
 }
 
+// Norm -> Mul(weight): the weight is the only vector, eps as for RMSNorm.
+int check_norm_mul(const convrot_pre *pre, int64_t K, PreOp *op, PreSpans *spans)
+{
+    if (pre->scale || pre->shift)
+        return CONVROT_EINVAL;
+    if ((pre->norm_weight && !aligned(pre->norm_weight, 16)) || !std::isfinite(pre->eps) ||
+        pre->eps < 0.0f)
+        return CONVROT_EINVAL;
+    if (K > quantize_max_k(K, true))
+        return CONVROT_EUNSUPPORTED;
+    op->kind = kPreNormMul;
+    op->norm_weight = pre->norm_weight;
+    op->eps = pre->eps;
+    spans->weight = span_of(pre->norm_weight, 4 * K);
+    return CONVROT_OK;
+}
+
 int check_pre(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, PreOp *op, PreSpans *spans)
 {
     *op = PreOp{};
@@ -211,6 +228,8 @@ int check_pre(const convrot_pre *pre, int64_t M, int64_t K, int x_dtype, PreOp *
         return CONVROT_OK;
     if (pre->kind == CONVROT_PRE_GATED_ACT)
         return check_gated_act(pre, M, K, x_dtype, op, spans);
+    if (pre->kind == CONVROT_PRE_NORM_MUL)
+        return check_norm_mul(pre, K, op, spans);
     if (pre->kind != CONVROT_PRE_MODULATE && pre->kind != CONVROT_PRE_RMSNORM_MODULATE)
         return CONVROT_EUNSUPPORTED;
     const bool rms = pre->kind == CONVROT_PRE_RMSNORM_MODULATE;

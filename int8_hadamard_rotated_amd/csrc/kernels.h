@@ -33,15 +33,15 @@ inline int64_t quantize_max_k(int64_t K, bool rmsnorm = false)
 }
 
 // Producer applied to each widened input element before the rotation.
-enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2, kPreGatedAct = 3 };
+enum PreKind : int { kPreNone = 0, kPreModulate = 1, kPreRmsNormModulate = 2, kPreGatedAct = 3, kPreNormMul = 4 };
 enum ActKind : int { kActSilu = 1, kActSigmoid = 2 };
 
 struct PreOp {
     int kind = kPreNone;
     const float *scale = nullptr;         // per-channel [K] or null (no modulation), 16-byte aligned
     const float *shift = nullptr;         // per-channel [K] or null (needs scale)
-    const float *norm_weight = nullptr;   // kPreRmsNormModulate: per-channel [K] or null
-    float eps = 0.0f;                     // kPreRmsNormModulate
+    const float *norm_weight = nullptr;   // kPreRmsNormModulate, kPreNormMul: per-channel [K] or null
+    float eps = 0.0f;                     // kPreRmsNormModulate, kPreNormMul
     const void *up = nullptr;             // kPreGatedAct: [M][ld_up], X's dtype
     int64_t ld_up = 0;
     int act = 0;                          // kPreGatedAct: ActKind

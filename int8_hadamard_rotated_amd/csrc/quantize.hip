@@ -13,6 +13,9 @@
 //   x  = fl(x * r) [* w]                   (optional RMSNorm -> Mul(weight)
 //                                           ahead of Modulate, same page and
 //                                           section; r per row, see below)
+//   x  = fl(fl(x - mean) * r) [* w]        (or Norm -> Mul(weight), same page
+//                                           and section; mean and r per row,
+//                                           see below)
 //   x  = x * alpha                         (multiply only when alpha != 1)
 //   y  = x R_G per contiguous G-group       (R_G = H4^(x)n, G = 4^n)
 //   m  = max |y| over the whole row
@@ -69,6 +72,10 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kQuadPermXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadPermXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+// The row normalization ahead of the quantizer: none, RMSNorm (root mean
+// square), or Norm (mean and variance).
+enum NormKind : int { kNormNone = 0, kNormRms = 1, kNormMean = 2 };
 
 template <int CTRL>
 __device__ __forceinline__ float quad_swap(float x)
@@ -266,14 +273,14 @@ __device__ __forceinline__ float sqrt_rn(float x)
     return s;
 }
 
-// RMSNorm's sums of squares for the quad's 64-feature blocks (block b = chunks
-// 2b and 2b+1): the pairwise tree of the 64 squares, adjacent pairs first.
-// Its levels are the element index bits: 0..2 in the chunk, 3 = lane bit 0,
-// 4 = chunk bit 0, 5 = lane bit 1; IEEE addition being commutative, both
-// lanes of a DPP pair hold the same bits.  Every lane of the quad ends with
-// every block sum.
-template <int NC>
-__device__ __forceinline__ void block_sums_sq(const float (&v)[NC][8], float (&bs)[NC / 2])
+// The normalizations' sums for the quad's 64-feature blocks (block b = chunks
+// 2b and 2b+1): the pairwise tree of the 64 values (SQ: of their squares),
+// adjacent pairs first.  Its levels are the element index bits: 0..2 in the
+// chunk, 3 = lane bit 0, 4 = chunk bit 0, 5 = lane bit 1; IEEE addition being
+// commutative, both lanes of a DPP pair hold the same bits.  Every lane of the
+// quad ends with every block sum.
+template <int NC, bool SQ>
+__device__ __forceinline__ void block_sums(const float (&v)[NC][8], float (&bs)[NC / 2])
 {
 #pragma unroll
     for (int b = 0; b < NC / 2; ++b) {
@@ -284,7 +291,7 @@ __device__ __forceinline__ void block_sums_sq(const float (&v)[NC][8], float (&b
             float q[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p)
-                q[p] = x[p] * x[p];
+                q[p] = SQ ? x[p] * x[p] : x[p];
             const float a0 = q[0] + q[1], a1 = q[2] + q[3], a2 = q[4] + q[5], a3 = q[6] + q[7];
             const float s8 = (a0 + a1) + (a2 + a3);
             s16[h] = s8 + quad_swap<kQuadPermXor1>(s8);
@@ -462,13 +469,16 @@ __device__ __forceinline__ void weight8_lds(float (&v)[8], const float *w, int c
 constexpr int kParamLdsBytes = 48 * 1024;
 
 //
-// RMSNorm (RMS = true) takes two more workgroup phases before the Modulate:
-// each quad stores its 64-feature block sums of squares in LDS; one lane per
-// row adds the row's K/64 block sums left to right and forms
+// RMSNorm (NRM = kNormRms) takes two more workgroup phases before the
+// Modulate: each quad stores its 64-feature block sums of squares in LDS; one
+// lane per row adds the row's K/64 block sums left to right and forms
 // r = fl(1 / fl(sqrt(fl(fl(S / K) + eps)))) with correctly rounded operations;
-// every lane then scales its values by its row's r (and the weight).
+// every lane then scales its values by its row's r (and the weight).  Norm
+// (NRM = kNormMean) first takes the same two phases over the values
+// themselves, mean = fl(S1 / K), and centres every value on it, so that the
+// squares are the deviations' and S / K is the variance.
 //
-// With RMSNorm or a gated activation the workgroup has at most 512 threads
+// With a row normalization or a gated activation the workgroup has at most 512 threads
 // (two waves per SIMD), so that the row data, the block sums or the exp's
 // binary64 temporaries fit in registers.
 //
@@ -489,8 +499,9 @@ constexpr int kParamLdsBytes = 48 * 1024;
 template <bool SCALED, int MOD, bool RMS, bool PS>
 constexpr int kQuantizeWaves = (RMS && PS && MOD == 2 && !SCALED) ? 3 : 1;
 
-template <typename XT, int G, int NC, bool SCALED, int MOD, bool RMS, int ACT, bool PS, bool LS>
-__global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024, (kQuantizeWaves<SCALED, MOD, RMS, PS>)) void quantize_rows_kernel(
+template <typename XT, int G, int NC, bool SCALED, int MOD, int NRM, int ACT, bool PS, bool LS>
+__global__ __launch_bounds__((NRM != kNormNone || ACT != 0) ? 512 : 1024,
+                             (kQuantizeWaves<SCALED, MOD, NRM != kNormNone, PS>)) void quantize_rows_kernel(
     const XT *__restrict__ X, int64_t M, int64_t M_pad, int64_t K, int64_t ldx, float alpha,
     const float *__restrict__ mod_scale, const float *__restrict__ mod_shift,
     const float *__restrict__ norm_weight, float eps, const XT *__restrict__ up, int64_t ld_up,
@@ -499,6 +510,8 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024, (kQuantizeWaves<SCA
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
     static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    constexpr bool RMS = NRM != kNormNone;               // a row normalization (either kind)
+    static_assert(NRM != kNormMean || MOD == 0, "Norm -> Mul has no Modulate");
     constexpr int kBlocks = NC / 2;                      // 64-feature blocks per quad span
     __shared__ unsigned row_max[256];
     __shared__ float norm_part[RMS ? 256 * kBlocks : 1];
@@ -641,9 +654,41 @@ __global__ __launch_bounds__((RMS || ACT != 0) ? 512 : 1024, (kQuantizeWaves<SCA
     }
     if constexpr (RMS) {
         const int row_blocks = quads_per_row * kBlocks;
+        if constexpr (NRM == kNormMean) {
+            // Norm: the row mean first, summed in the same tree (block sums,
+            // then the row's block sums left to right), and every value
+            // centred on it; the squares below are then the deviations'.
+            // norm_part and norm_r are next written after the barrier that
+            // follows every read here.
+            if (live) {
+                float bs[kBlocks];
+                block_sums<NC, false>(v, bs);
+                if ((tid & 3) == 0)
+#pragma unroll
+                    for (int b = 0; b < kBlocks; ++b)
+                        norm_part[row_local * row_blocks + q_in_row * kBlocks + b] = bs[b];
+            }
+            __syncthreads();
+            if (tid < rows_per_wg) {
+                const float *bp = norm_part + tid * row_blocks;
+                float sum = bp[0];
+                for (int b = 1; b < row_blocks; ++b)
+                    sum = sum + bp[b];
+                norm_r[tid] = __fdiv_rn(sum, (float)K);
+            }
+            __syncthreads();
+            if (live) {
+                const float mean = norm_r[row_local];
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        v[c][p] = v[c][p] - mean;
+            }
+        }
         if (live) {
             float bs[kBlocks];
-            block_sums_sq<NC>(v, bs);
+            block_sums<NC, true>(v, bs);
             if ((tid & 3) == 0)
 #pragma unroll
                 for (int b = 0; b < kBlocks; ++b)
@@ -1002,10 +1047,11 @@ int plan_rows(int qr, int max_threads)
     return rows;
 }
 
-template <typename XT, int G, int NC, int MOD, bool RMS, int ACT>
+template <typename XT, int G, int NC, int MOD, int NRM, int ACT>
 hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float alpha, const PreOp &pre,
                   void *packed, hipStream_t stream)
 {
+    constexpr bool RMS = NRM != kNormNone;
     const int64_t m_pad = (M + 3) / 4 * 4;
     const int qr = (int)(K / (32 * NC));
     constexpr int kMaxThreads = (RMS || ACT != 0) ? 512 : 1024;
@@ -1057,19 +1103,19 @@ hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float 
             // beyond the default LDS limit of a launch: raise the kernel's
             // dynamic maximum first, and make no launch if that fails
             const void *fn =
-                alpha != 1.0f ? reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT, PS, LS>)
-                              : reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT, PS, LS>);
+                alpha != 1.0f ? reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, true, MOD, NRM, ACT, PS, LS>)
+                              : reinterpret_cast<const void *>(&quantize_rows_kernel<XT, G, NC, false, MOD, NRM, ACT, PS, LS>);
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess)
                 return e;
         }
         if (alpha != 1.0f)
-            hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, RMS, ACT, PS, LS>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, true, MOD, NRM, ACT, PS, LS>), dim3((unsigned)blocks),
                                dim3(threads), lds, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
                                alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
                                qr, rows, wave_store);
         else
-            hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, RMS, ACT, PS, LS>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((quantize_rows_kernel<XT, G, NC, false, MOD, NRM, ACT, PS, LS>), dim3((unsigned)blocks),
                                dim3(threads), lds, stream, static_cast<const XT *>(X), M, m_pad, K, ldx,
                                alpha, pre.scale, pre.shift, pre.norm_weight, pre.eps, up, pre.ld_up, Q, S,
                                qr, rows, wave_store);
@@ -1091,41 +1137,41 @@ hipError_t launch_typed(const void *X, int64_t M, int64_t K, int64_t ldx, float 
     return go(std::false_type{}, std::false_type{});
 }
 
-template <typename XT, int NC, int MOD, bool RMS, int ACT>
+template <typename XT, int NC, int MOD, int NRM, int ACT>
 hipError_t launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                      const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
-    case 4: return launch_typed<XT, 4, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
-    case 16: return launch_typed<XT, 16, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
-    case 64: return launch_typed<XT, 64, NC, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+    case 4: return launch_typed<XT, 4, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+    case 16: return launch_typed<XT, 16, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+    case 64: return launch_typed<XT, 64, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
     default:
         if constexpr (NC == 8)
-            return launch_typed<XT, 256, 8, MOD, RMS, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
+            return launch_typed<XT, 256, 8, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
         return hipErrorInvalidValue;   // not reached: the API admits G = 256 only with K % 256 == 0
     }
 }
 
-template <typename XT, int MOD, bool RMS, int ACT>
+template <typename XT, int MOD, int NRM, int ACT>
 hipError_t launch_dtype(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                         const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (K % 256 == 0)
-        return launch_nc<XT, 8, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_nc<XT, 8, MOD, NRM, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
     if (K % 128 == 0)
-        return launch_nc<XT, 4, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    return launch_nc<XT, 2, MOD, RMS, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_nc<XT, 4, MOD, NRM, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_nc<XT, 2, MOD, NRM, ACT>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
-template <typename XT, bool RMS>
+template <typename XT, int NRM>
 hipError_t launch_mod(int G, const void *X, int64_t M, int64_t K, int64_t ldx, float alpha,
                       const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (pre.scale && pre.shift)
-        return launch_dtype<XT, 2, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_dtype<XT, 2, NRM, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
     if (pre.scale)
-        return launch_dtype<XT, 1, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    return launch_dtype<XT, 0, RMS, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_dtype<XT, 1, NRM, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_dtype<XT, 0, NRM, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 template <typename XT>
@@ -1133,12 +1179,14 @@ hipError_t launch_pre(int G, const void *X, int64_t M, int64_t K, int64_t ldx, f
                       const PreOp &pre, void *packed, hipStream_t stream)
 {
     if (pre.kind == kPreRmsNormModulate)
-        return launch_mod<XT, true>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_mod<XT, kNormRms>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    if (pre.kind == kPreNormMul)
+        return launch_dtype<XT, 0, kNormMean, 0>(G, X, M, K, ldx, alpha, pre, packed, stream);
     if (pre.kind == kPreGatedAct && pre.act == kActSilu)
-        return launch_dtype<XT, 0, false, kActSilu>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_dtype<XT, 0, kNormNone, kActSilu>(G, X, M, K, ldx, alpha, pre, packed, stream);
     if (pre.kind == kPreGatedAct)
-        return launch_dtype<XT, 0, false, kActSigmoid>(G, X, M, K, ldx, alpha, pre, packed, stream);
-    return launch_mod<XT, false>(G, X, M, K, ldx, alpha, pre, packed, stream);
+        return launch_dtype<XT, 0, kNormNone, kActSigmoid>(G, X, M, K, ldx, alpha, pre, packed, stream);
+    return launch_mod<XT, kNormNone>(G, X, M, K, ldx, alpha, pre, packed, stream);
 }
 
 // y may be x (each lane reads its element before writing it).

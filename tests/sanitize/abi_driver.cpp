@@ -81,6 +81,18 @@ static void quantize()
     EXPECT(g_log.q_pre == convrot_detail::kPreRmsNormModulate);
     pre.eps = -1.0f;
     EXPECT(convrot_quantize_rows_pre(at(0), CONVROT_F32, 9, 3072, 3072, &pre, 256, 1.0f, at(64), nullptr) == CONVROT_EINVAL);
+    convrot_pre nm{};
+    nm.kind = CONVROT_PRE_NORM_MUL;
+    nm.norm_weight = at_t<const float>(202);
+    nm.eps = 1e-6f;
+    reset();
+    EXPECT(convrot_quantize_rows_pre(at(0), CONVROT_BF16, 9, 3072, 3072, &nm, 256, 1.0f, at(64), nullptr) == CONVROT_OK);
+    EXPECT(g_log.q_pre == convrot_detail::kPreNormMul);
+    nm.scale = at_t<const float>(200);
+    EXPECT(convrot_quantize_rows_pre(at(0), CONVROT_BF16, 9, 3072, 3072, &nm, 256, 1.0f, at(64), nullptr) == CONVROT_EINVAL);
+    nm.scale = nullptr;
+    nm.norm_weight = at_t<const float>(64);          // packed over the weight
+    EXPECT(convrot_quantize_rows_pre(at(0), CONVROT_BF16, 9, 3072, 3072, &nm, 256, 1.0f, at(64), nullptr) == CONVROT_EOVERLAP);
     convrot_pre act{};
     act.kind = CONVROT_PRE_GATED_ACT;
     act.up = at(300);

@@ -153,6 +153,17 @@ def test_producer_validation(lib):
     assert qpre(lib, kind=rms, w=w + 8) == EINVAL
     assert qpre(lib, kind=rms, w=BASE + 64 * MB + 1024) == EOVL        # packed overlaps the weight
     assert qpre(lib, kind=rms, w=w, K=32768 + 256) == EUNSUP
+    # Norm -> Mul(weight): no scale or shift, the same eps, weight and row rules
+    nm = cr.PRE_NORM_MUL
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=w, eps=1e-6, M=0) == OK
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=0, eps=0.0, M=0) == OK       # Norm alone
+    assert qpre(lib, kind=nm, sh=0, w=w) == EINVAL                      # a scale
+    assert qpre(lib, kind=nm, sc=0, w=w) == EINVAL                      # a shift
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=w, eps=-1e-6) == EINVAL
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=w, eps=float("nan")) == EINVAL
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=w + 8) == EINVAL
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=BASE + 64 * MB + 1024) == EOVL   # packed on the weight
+    assert qpre(lib, kind=nm, sc=0, sh=0, w=w, K=32768 + 256) == EUNSUP
     # gated activation: a second input with X's dtype, aligned, with a valid
     # stride, that packed does not overlap; SiLU or Sigmoid; same row limit
     def qact(up=BASE + 100 * MB, ld=256, act=cr.ACT_SILU, M=8, K=256, packed=BASE + 64 * MB):

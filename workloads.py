@@ -30,7 +30,8 @@ Recipe, per workload (fixed draw order):
         residual = rng.standard_normal((M, N), float32), in the output dtype
     when the workload has a gated activation producer (X is the gate):
         up = rng.standard_normal((M, K), float32), outliers as for X, same dtype
-    when the workload has an RMSNorm -> Mul(weight) producer (eps 1e-6):
+    when the workload has an RMSNorm -> Mul(weight) or a Norm -> Mul(weight)
+    producer (eps 1e-6):
         norm_weight = 1 + rng.standard_normal(K, float32) * 0.1
     when the workload has a Modulate producer (per-channel vectors, as the
     adaLN modulation of a DiT block supplies them):
@@ -64,7 +65,8 @@ class Workload:
     w_bits: int = 8                   # 4: convrot_w4a4 packed weights
     gated: bool = False               # a gated-residual epilogue after the linear
     rmsnorm: bool = False             # RMSNorm -> Mul(weight) ahead of the Modulate
-    rms_eps: float = 1e-6
+    norm: bool = False                # Norm (mean and variance) -> Mul(weight) ahead of the rotation
+    rms_eps: float = 1e-6             # eps of either normalization
     glu: int = 0                      # 1 SiLU, 2 Sigmoid: fl(act(X) * up) ahead of the rotation
     swiglu: bool = False              # the two linears are a SwiGLU pair (gate, up), bias-free
     note: str = ""
@@ -90,6 +92,9 @@ WORKLOADS = {
     "mlp_up_rms": Workload("mlp_up_rms", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=8,
                            modulate=True, rmsnorm=True,
                            note="DiT MLP up-projection with RMSNorm -> Mul(weight) -> Modulate fused"),
+    "mlp_up_norm": Workload("mlp_up_norm", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=11,
+                            norm=True,
+                            note="DiT MLP up-projection with Norm -> Mul(weight) fused"),
     "mlp_up_w4": Workload("mlp_up_w4", 4096, 3072, 12288, 256, BF16, BF16, (1.0,), seed=6,
                           w_bits=4, note="DiT MLP up-projection with convrot_w4a4 weights"),
     "proj_gated": Workload("proj_gated", 4096, 3072, 3072, 256, BF16, BF16, (1.0,), seed=7,
@@ -148,7 +153,7 @@ class Inputs:
     W: list = field(default_factory=list)   # float32 [N,K] per linear
     b: list = field(default_factory=list)   # float32 [N] per linear
     s_w: list = field(default_factory=list) # float32 [N] per linear (4-bit weights only)
-    norm_weight: np.ndarray | None = None   # float32 [K] (RMSNorm producer)
+    norm_weight: np.ndarray | None = None   # float32 [K] (RMSNorm or Norm producer)
     up: np.ndarray | None = None            # like X, [M,K] (gated activation producer)
     mod_scale: np.ndarray | None = None     # float32 [K] (Modulate producer)
     mod_shift: np.ndarray | None = None     # float32 [K]
@@ -176,7 +181,7 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
         inp.b.append(b)
     if w.glu:
         inp.up = gaussian_activations(rng, rows, w.K, w.outlier_p, w.outlier_f, w.x_dtype)
-    if w.rmsnorm:
+    if w.rmsnorm or w.norm:
         inp.norm_weight = norm_weight(rng, w.K)
     if w.modulate:
         inp.mod_scale, inp.mod_shift = modulation(rng, w.K)
@@ -187,7 +192,7 @@ def make_inputs(w: Workload, seed: int | None = None, M: int | None = None) -> I
 
 
 def norm_weight(rng: np.random.Generator, K: int, sigma: float = 0.1):
-    """RMSNorm weight 1 + N(0, sigma), fp32 [K]."""
+    """Normalization weight 1 + N(0, sigma), fp32 [K]."""
     return np.float32(1.0) + rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
 
 
