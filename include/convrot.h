@@ -98,7 +98,8 @@ size_t convrot_packed_bytes(int64_t M, int64_t K);
  * "Runtime activation quantization", the per-row scale and codes; packed as
  * convrot_packed_bytes describes).
  *   X           [M][ldx] f32 or bf16 (x_dtype), first K columns used
- *   group_size  G, rotation group (power of four dividing K)
+ *   group_size  G, rotation group (power of four dividing K: 1, 4, 16, 64 or
+ *               256; G = 1 is the identity, per-row quantization alone)
  *   input_scale alpha > 0, finite; X is multiplied by it before the rotation
  *   packed      convrot_packed_bytes(M, K) bytes, written entirely (pad rows
  *               and pad scales included); must not overlap X

@@ -76,11 +76,11 @@ bool scale_ok(float a) { return std::isfinite(a) && a > 0.0f; }
 int hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_EHIP; }
 
 // Group size rule of the convrot checkpoint format (a power of four dividing
-// K), restricted to the groups this library implements, plus the MFMA K
-// granularity of 64.
+// K), restricted to the groups this library implements (1 = no rotation up to
+// 256), plus the MFMA K granularity of 64.
 int check_quantizer_shape(int64_t K, int G)
 {
-    if (!(G == 4 || G == 16 || G == 64 || G == 256))
+    if (!(G == 1 || G == 4 || G == 16 || G == 64 || G == 256))
         return CONVROT_EUNSUPPORTED;
     if (K % 64 != 0 || K % G != 0)
         return CONVROT_EUNSUPPORTED;

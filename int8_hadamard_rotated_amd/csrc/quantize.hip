@@ -185,11 +185,14 @@ __device__ __forceinline__ int chunk_offset(int j0, int j1, int c)
 template <int G, int NC, bool LS = false>
 __device__ __forceinline__ void rotate_span(float (&v)[NC][8])
 {
+    // G = 1 (4^0): no digit, the identity
     // digit 0 (stride 1)
+    if constexpr (G >= 4) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
-        h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
+        for (int c = 0; c < NC; ++c) {
+            h4_local(v[c][0], v[c][1], v[c][2], v[c][3]);
+            h4_local(v[c][4], v[c][5], v[c][6], v[c][7]);
+        }
     }
     // digit 1 (stride 4): low bit p>>2, high bit lane bit 0
     if constexpr (G >= 16) {
@@ -509,7 +512,7 @@ __global__ __launch_bounds__((NRM != kNormNone || ACT != 0) ? 512 : 1024,
     int wave_store)
 {
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
-    static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    static_assert(G == 1 || G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
     constexpr bool RMS = NRM != kNormNone;               // a row normalization (either kind)
     static_assert(NRM != kNormMean || MOD == 0, "Norm -> Mul has no Modulate");
     constexpr int kBlocks = NC / 2;                      // 64-feature blocks per quad span
@@ -843,7 +846,7 @@ __global__ __launch_bounds__(256) void quantize_rows_staged(
     constexpr bool MULTI = NS > 1;
     static_assert(NS == 1 || (NS == 2 && MOD == 0 && !SCALED), "two scales: plain rows, scales in outs");
     static_assert(NC == 2 || NC == 4 || NC == 8, "chunks per lane");
-    static_assert(G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
+    static_assert(G == 1 || G == 4 || G == 16 || G == 64 || (G == 256 && NC == 8), "group size vs span");
     constexpr int kPC = 2;                                // 16-B pieces per 8-element chunk
     constexpr int kQuadPieces = 4 * NC * kPC;            // 16-B input pieces per quad span
     constexpr int kWavePieces = 16 * kQuadPieces;        // per wave
@@ -1142,6 +1145,7 @@ hipError_t launch_nc(int G, const void *X, int64_t M, int64_t K, int64_t ldx, fl
                      const PreOp &pre, void *packed, hipStream_t stream)
 {
     switch (G) {
+    case 1: return launch_typed<XT, 1, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
     case 4: return launch_typed<XT, 4, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
     case 16: return launch_typed<XT, 16, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
     case 64: return launch_typed<XT, 64, NC, MOD, NRM, ACT>(X, M, K, ldx, alpha, pre, packed, stream);
@@ -1221,6 +1225,7 @@ hipError_t launch_scales_nc(int G, const float *X, int64_t M, int64_t K, int64_t
                             int64_t m_pad, int qr, int rows, hipStream_t stream)
 {
     switch (G) {
+    case 1: return launch_staged_scales<1, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
     case 4: return launch_staged_scales<4, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
     case 16: return launch_staged_scales<16, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);
     case 64: return launch_staged_scales<64, NC>(X, M, K, ldx, outs, m_pad, qr, rows, stream);

@@ -216,6 +216,26 @@ def pin_quantizer_exact(o):
             assert int(p.q[r, i]) == want, f"code ({r},{i}): {p.q[r, i]} vs {want}"
 
 
+def pin_quantizer_group_one(o):
+    """G = 1 (4^0) is the identity rotation: codes and scales of the widened
+    input itself against exact rational arithmetic with binary32 rounding,
+    for binary32 and bf16 rows, and the same packed bytes as rotating by
+    nothing (the oracle's rotation at G = 1 returns its input)."""
+    rng = np.random.default_rng(26)
+    X = workloads.gaussian_activations(rng, 3, 192, 0.02, 20.0, workloads.F32)
+    Xb = workloads.f32_to_bf16_bits(X)
+    for src, xw in ((X, X), (Xb, workloads.bf16_bits_to_f32(Xb))):
+        p = o.quantize_rows(src, 1)
+        for r in range(3):
+            m = F(np.max(np.abs(xw[r])))
+            assert F(p.s[r]) == rne_f32(m / 127), f"G=1 scale row {r}"
+            inv = rne_f32(Fraction(127) / m)
+            for i in range(192):
+                want = max(-127, min(127, round_half_even(rne_f32(F(xw[r, i]) * inv))))
+                assert int(p.q[r, i]) == want, f"G=1 code ({r},{i}): {p.q[r, i]} vs {want}"
+    assert np.array_equal(o.rotate_rows(X, 1), X)
+
+
 def pin_tie_row(o):
     """Rounding rule, pinned on constructed ties (golden/tie_row_g16.txt)."""
     vals, codes = load_tie_row()

@@ -77,7 +77,8 @@ def q(lib, X=BASE, dt=cr.F32, M=8, K=256, ldx=None, G=16, a=1.0, packed=BASE + 6
 
 def test_quantize_validation(lib):
     assert q(lib, G=8) == EUNSUP
-    assert q(lib, G=1) == EUNSUP
+    assert q(lib, G=2) == EUNSUP
+    assert q(lib, G=1, M=0) == OK                        # 4^0: no rotation
     assert q(lib, G=1024, K=2048) == EUNSUP
     assert q(lib, K=100, G=4) == EUNSUP                  # K % 64
     assert q(lib, K=320, G=256) == EUNSUP                # K % G

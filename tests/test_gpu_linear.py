@@ -285,6 +285,22 @@ def test_shared_mixed_scales_big_grid(orc):
         assert_bits_equal(y, want, f"alpha={a}")
 
 
+@pytest.mark.parametrize("dtype", [workloads.F32, workloads.BF16])
+def test_fused_group_one(orc, dtype):
+    """G = 1 (no rotation) through the fused entry, weights prepared at G = 1
+    too, on a ragged shape of both tile sizes' grids, against the oracle."""
+    rng = np.random.default_rng(81)
+    for (M, K, N) in ((257, 512, 300), (1030, 768, 3072 + 17)):
+        X = workloads.gaussian_activations(rng, M, K, 0.005, 30.0, dtype)
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, 1, threads=THREADS)
+        for a in (1.0, 0.3):
+            say("fused G=1", M, K, N, dtype, a)
+            Y = host(cr.convrot_int8_linear(dev_x(X), 1, a, dev(Qw), dev(sw), dev(b)))
+            want = orc.linear(X, 1, Qw, sw, b, a, threads=THREADS)
+            check_y(Y, want, oracle.F32, f"G=1 M={M} N={N} {dtype} alpha={a}")
+
+
 def test_int8_linear_strided_output(orc):
     """ldy > N, and an output whose rows do not allow vector stores."""
     rng = np.random.default_rng(5)

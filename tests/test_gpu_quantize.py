@@ -43,7 +43,7 @@ EDGE_SHAPES = [(1, 64), (3, 128), (4, 192), (5, 256), (127, 320), (13, 512), (17
                (2, 65536)]
 
 
-@pytest.mark.parametrize("G", [4, 16, 64, 256])
+@pytest.mark.parametrize("G", [1, 4, 16, 64, 256])
 @pytest.mark.parametrize("dtype", [workloads.F32, workloads.BF16])
 def test_edge_shapes(orc, G, dtype):
     rng = np.random.default_rng(100 + G)
@@ -76,7 +76,9 @@ SCALES_CASES = [(4096, 3072, workloads.F32, 256, (1.0, 0.5)),
                 (77, 1024, workloads.F32, 256, (1.0, 0.3, 0.5, 0.7, 1.3, 2.0, 0.11, 3.7, 0.25, 5.0, 0.9,
                                                 1.1, 0.6, 2.5, 0.45, 8.0)),
                 (50, 768, workloads.BF16, 64, (0.3, 0.7, 1.0, 1.9, 0.5)),
-                (5, 4096, workloads.F32, 16, (0.3, 0.7, 1.0))]
+                (5, 4096, workloads.F32, 16, (0.3, 0.7, 1.0)),
+                (33, 1024, workloads.F32, 1, (1.0, 0.3)),
+                (21, 640, workloads.BF16, 1, (0.3, 1.0))]
 
 
 @pytest.mark.parametrize("M,K,dtype,G,scales", SCALES_CASES)
