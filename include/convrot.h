@@ -342,7 +342,10 @@ int convrot_int8_gemm_i32(const int8_t *Qx, const int8_t *Qw, int64_t M, int64_t
  * device [M][ld_residual] tensor in the output dtype (bf16 widened exactly).
  * The residual may be Y itself (same base and row stride: an exact in-place
  * residual); any other overlap with Y, or a gate overlapping Y, is
- * CONVROT_EOVERLAP. */
+ * CONVROT_EOVERLAP.  The chain's optional [Concat] needs no kernel of its
+ * own: Y and ldy place the rows in their slice of the concatenated tensor
+ * (Y at the slice's first element, ldy the full row length), and nothing
+ * outside the M x N slice is written. */
 typedef enum { CONVROT_POST_NONE = 0, CONVROT_POST_GATED_RESIDUAL = 1 } convrot_post_kind;
 
 typedef struct {

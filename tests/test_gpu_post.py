@@ -96,6 +96,42 @@ def test_gated_residual_strided(orc):
     assert np.all(got[:, N:] == -7.0), "wrote past N"
 
 
+@pytest.mark.parametrize("col0,extra", [(256, 256), (64, 3)])
+def test_gated_residual_concat(orc, col0, extra):
+    """The chain's optional [Concat] (page "ggml operator extensions", section
+    "sd.cpp integration": INT8 GEMM -> [Scale] -> Mul(gate) -> Add(residual)
+    -> [Concat]): the result written straight into its slice of the
+    concatenated tensor through Y and ldy, along the features (a column
+    block of a wider row) and along the tokens (a row block), every other
+    element left as it was.  col0 = 256 keeps 16-byte rows (vector stores),
+    col0 = 64 with an odd width does not; 171 tiles of 256 x 256."""
+    import torch
+    rng = np.random.default_rng(75 + col0)
+    M, K, N = 2051, 256, 4613
+    p, Qw, sw, b, A, gate = case(rng, orc, M, K, N, G=256)
+    R = workloads.gaussian_activations(rng, M, N, 0.0, 1.0, workloads.BF16)
+    Yf = orc.epilogue(A, p.s, sw, b, 1.0, oracle.F32, threads=THREADS)
+    want = orc.gated_residual(Yf, gate, R, 0.37, oracle.BF16, threads=THREADS)
+    post = cr.GatedResidual(dev(gate), dev_x(R), 0.37)
+    # along the features: [other | this | other]
+    width = col0 + N + extra
+    D = torch.full((M, width), 3.0, dtype=torch.bfloat16, device="cuda:0")
+    say("gated concat columns", col0, width)
+    cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), 1.0, post,
+                        Y=D[:, col0:col0 + N])
+    got = host(D)
+    check_y(np.ascontiguousarray(got[:, col0:col0 + N]), want, oracle.BF16, "concat columns")
+    assert np.all(got[:, :col0] == 0x4040) and np.all(got[:, col0 + N:] == 0x4040), "wrote outside its columns"
+    # along the tokens: rows [r0, r0 + M) of a taller tensor
+    r0 = 5
+    T = torch.full((r0 + M + 2, N), 3.0, dtype=torch.bfloat16, device="cuda:0")
+    say("gated concat rows", r0)
+    cr.int8_linear_post(dev(p.q), dev(p.s), dev(Qw), dev(sw), dev(b), 1.0, post, Y=T[r0:r0 + M])
+    got = host(T)
+    check_y(np.ascontiguousarray(got[r0:r0 + M]), want, oracle.BF16, "concat rows")
+    assert np.all(got[:r0] == 0x4040) and np.all(got[r0 + M:] == 0x4040), "wrote outside its rows"
+
+
 def test_gated_residual_workload(orc):
     """The DiT output projection with its gated residual in place, at full
     size from a GPU-quantized packed tensor, every output compared."""
