@@ -157,3 +157,75 @@ def test_shared_entry_replays(orc):
                 for d, ((Qw, sw, b), a) in enumerate(zip(preps, scales)):
                     want = orc.linear(X, G, Qw, sw, b, a, threads=THREADS)
                     check_y(eager[d], want, oracle.F32, f"eager linear {d} input {j}")
+
+
+def test_scales_grouped_and_norm_replays(orc):
+    """Two chains in one graph: the literal qkv-style step (one
+    convrot_quantize_rows_scales call for input scales 1 and 0.3 on binary32
+    rows, then one int8_linear_grouped launch whose second linear reads the
+    0.3 tensor) and a Norm -> Mul(weight) producer pass at G = 1 feeding
+    int8_linear; every replay against the eager calls, those against the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(81)
+    M, K, G = 517, 1024, 256
+    Ns, scales = [384, 200], [1.0, 0.3]
+    Xs = [workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.F32) for _ in range(2)]
+    Zs = [workloads.gaussian_activations(rng, M, K, 0.005, 30.0, workloads.BF16) for _ in range(2)]
+    preps, lins, Ys = [], [], []
+    for a, N in zip(scales, Ns):
+        W, b = workloads.gaussian_weights(rng, N, K)
+        Qw, sw = orc.weight_prep(W, G, threads=THREADS)
+        preps.append((Qw, sw, b))
+        Ys.append(torch.empty((M, N), dtype=torch.float32, device="cuda:0"))
+        lins.append(dict(Qw=dev(Qw), s_w=dev(sw), bias=dev(b), input_scale=a))
+    W1, b1 = workloads.gaussian_weights(rng, 300, K)
+    Q1, s1 = orc.weight_prep(W1, 1, threads=THREADS)
+    Q1d, s1d, b1d = dev(Q1), dev(s1), dev(b1)
+    nw = workloads.norm_weight(rng, K)
+    norm = cr.NormMul(1e-6, dev(nw))
+    pb = cr.convrot_packed_bytes(M, K)
+    Xd, Zd = dev_x(Xs[0]), dev_x(Zs[0])
+
+    def chain(pks, ys, pk3, y3):
+        cr.convrot_quantize_rows_scales(Xd, G, scales, packed=pks)
+        qx, sx = cr.packed_parts(pks[0], M, K)
+        q2, s2 = cr.packed_parts(pks[1], M, K)
+        cr.int8_linear_grouped(qx, sx, [dict(lins[0], Y=ys[0]), dict(lins[1], Y=ys[1], Qx=q2, s_x=s2)], M=M)
+        cr.convrot_quantize_rows_pre(Zd, norm, 1, packed=pk3)
+        q3, s3 = cr.packed_parts(pk3, M, K)
+        cr.int8_linear(q3, s3, Q1d, s1d, b1d, 1.0, Y=y3, M=M)
+
+    def bufs():
+        return ([torch.empty(pb, dtype=torch.uint8, device="cuda:0") for _ in scales],
+                [torch.empty_like(y) for y in Ys], torch.empty(pb, dtype=torch.uint8, device="cuda:0"),
+                torch.empty((M, 300), dtype=torch.float32, device="cuda:0"))
+
+    cap_pks, _, cap_pk3, cap_y3 = bufs()
+    say("graph capture: scales + grouped, norm at G=1", M, K, Ns)
+    g = capture(lambda: chain(cap_pks, Ys, cap_pk3, cap_y3))
+    for rep in range(REPLAYS):
+        for j, (X, Z) in enumerate(zip(Xs, Zs)):
+            Xd.copy_(dev_x(X))
+            Zd.copy_(dev_x(Z))
+            e_pks, e_ys, e_pk3, e_y3 = bufs()
+            say("eager", rep, j)
+            chain(e_pks, e_ys, e_pk3, e_y3)
+            for y in Ys + [cap_y3]:
+                y.fill_(-7.0)
+            for pk in cap_pks + [cap_pk3]:
+                pk.fill_(0x5A)
+            say("replay", rep, j)
+            g.replay()
+            for d in range(2):
+                assert_bits_equal(host(cap_pks[d]), host(e_pks[d]), f"packed {d}, replay {rep} input {j}")
+                assert_bits_equal(host(Ys[d]), host(e_ys[d]), f"grouped linear {d}, replay {rep} input {j}")
+            assert_bits_equal(host(cap_pk3), host(e_pk3), f"norm packed, replay {rep} input {j}")
+            assert_bits_equal(host(cap_y3), host(e_y3), f"G=1 linear, replay {rep} input {j}")
+            if rep == 0:
+                for d, ((Qw, sw, b), a) in enumerate(zip(preps, scales)):
+                    want = orc.linear(X, G, Qw, sw, b, a, threads=THREADS)
+                    check_y(host(e_ys[d]), want, oracle.F32, f"eager grouped linear {d} input {j}")
+                want = orc.linear(orc.norm_rows(Z, 1e-6, nw, threads=THREADS), 1, Q1, s1, b1, 1.0,
+                                  threads=THREADS)
+                check_y(host(e_y3), want, oracle.F32, f"eager norm G=1 linear input {j}")
