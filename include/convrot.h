@@ -53,7 +53,7 @@
  *     error nothing is enqueued and a negative convrot_status is returned.
  *     Errors are never retried and there is no fallback to another device.
  *   - M = 0 or N = 0 is valid and enqueues nothing.
- *   - GPU support: G in {4, 16, 64, 256}; K a multiple of 64 and of G; the
+ *   - GPU support: G in {1, 4, 16, 64, 256}; K a multiple of 64 and of G; the
  *     quantizer needs K <= 65536, the contraction K <= 133120 (so that
  *     K * 127^2 < 2^31: codes are taken to lie in [-127, 127], as the
  *     quantizer produces).  Pointers to X, packed buffers, Q_x, Q_w and the
